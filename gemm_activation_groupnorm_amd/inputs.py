@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for the fused Linear -> Swish -> +bias -> GroupNorm path.
+
+This module only draws random numbers and rounds them to the storage type; it
+holds none of the method's arithmetic.  The tests feed the same arrays to the
+CPU oracle and to the HIP library; the benchmark uses it for its workload.
+
+Value distributions follow the transcript's problem (an nn.Linear with
+PyTorch's default uniform(-1/sqrt(K), 1/sqrt(K)) init for weight and bias, an
+external per-channel bias, and GroupNorm gamma/beta), perturbed so that every
+term of the forward is exercised:
+
+    x      ~ x_scale * N(0, 1)
+    W      ~ U(-1/sqrt(K), 1/sqrt(K))          [N, K], nn.Linear layout
+    b_lin  ~ U(-1/sqrt(K), 1/sqrt(K))          [N]
+    b_add  ~ 0.02 * N(0, 1)                    [N]
+    gamma  ~ 1 + 0.1 * N(0, 1)                 [N]
+    beta   ~ 0.1 * N(0, 1)                     [N]
+
+Draw order x, W, b_lin, b_add, gamma, beta from numpy's PCG64
+(``default_rng(seed)``), in float64, then rounded to float32 (round to nearest
+even).  For the bf16 workload x and W are further rounded from float32 to
+bfloat16 (round to nearest even); both sides then see the same bf16 values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    K: int
+    N: int
+    G: int
+    dtype: str          # "f32" or "bf16": storage type of x and W
+    seed: int
+    eps: float = 1e-5
+    x_scale: float = 1.0
+
+    @property
+    def channels_per_group(self) -> int:
+        return self.N // self.G
+
+    @property
+    def flops(self) -> int:
+        """GEMM flops, 2*M*N*K (the epilogue is not counted)."""
+        return 2 * self.M * self.N * self.K
+
+
+# The five workloads: tiny, small, the transcript's own shape in fp32 and in
+# bf16, and a wide-group shape (1024 channels per group).
+WORKLOADS = [
+    Workload("tiny_f32", 64, 32, 128, 8, "f32", 0),
+    Workload("small_f32", 1024, 256, 1024, 16, "f32", 1),
+    Workload("m32768_k1024_n4096_g64_f32", 32768, 1024, 4096, 64, "f32", 2),
+    Workload("m32768_k1024_n4096_g64_bf16", 32768, 1024, 4096, 64, "bf16", 3),
+    Workload("m16384_k2048_n8192_g8_f32", 16384, 2048, 8192, 8, "f32", 4, x_scale=2.0),
+]
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits.
+
+    Inputs are finite by construction, so NaN handling is not needed."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounding = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    return ((u + rounding) >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def make_inputs(M: int, K: int, N: int, seed: int, dtype: str = "f32",
+                x_scale: float = 1.0) -> Dict[str, np.ndarray]:
+    """Draw one input set.
+
+    Returns float32 arrays ``x, W, b_lin, b_add, gamma, beta``.  For
+    ``dtype == "bf16"`` also ``x_bf16, W_bf16`` (uint16 bit patterns) and
+    ``x, W`` hold the float32 widening of exactly those bf16 values.
+    """
+    rng = np.random.default_rng(seed)
+    bound = 1.0 / np.sqrt(K) if K > 0 else 0.0
+    x = (rng.standard_normal((M, K)) * x_scale).astype(np.float32)
+    W = rng.uniform(-bound, bound, (N, K)).astype(np.float32)
+    b_lin = rng.uniform(-bound, bound, N).astype(np.float32)
+    b_add = (rng.standard_normal(N) * 0.02).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(N)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    out = dict(x=x, W=W, b_lin=b_lin, b_add=b_add, gamma=gamma, beta=beta)
+    if dtype == "bf16":
+        xb = f32_to_bf16_bits(x)
+        Wb = f32_to_bf16_bits(W)
+        out.update(x_bf16=xb, W_bf16=Wb, x=bf16_bits_to_f32(xb), W=bf16_bits_to_f32(Wb))
+    elif dtype != "f32":
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    return out
+
+
+def workload_inputs(w: Workload) -> Dict[str, np.ndarray]:
+    return make_inputs(w.M, w.K, w.N, w.seed, w.dtype, w.x_scale)
+
+
+def get_workload(name_or_index) -> Workload:
+    if isinstance(name_or_index, int):
+        return WORKLOADS[name_or_index]
+    for w in WORKLOADS:
+        if w.name == name_or_index:
+            return w
+    raise KeyError(name_or_index)
+
+
+def sample_rows(M: int, count: int, seed: int = 12345) -> np.ndarray:
+    """Sorted, distinct row indices that always include the first and last row."""
+    count = min(count, M)
+    rng = np.random.default_rng(seed)
+    rows = set([0, M - 1])
+    rest = rng.choice(M, size=count, replace=False)
+    for r in rest:
+        if len(rows) >= count:
+            break
+        rows.add(int(r))
+    return np.array(sorted(rows), dtype=np.int64)

@@ -1,0 +1,141 @@
+"""fp64 CPU oracle for the fused Linear -> Swish -> +bias -> GroupNorm forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library (``gemm_activation_groupnorm_amd``) and neither imports the
+other; the seeded input generators live in a module of their own.
+
+What it computes (POPCORNBENCH transcript "Kimi-K2.6 l2_p37", the problem
+statement and the passages fixing the forward order):
+
+    z = x . W^T + b_lin              (nn.Linear, W stored [N, K])
+    s = sigmoid(z) * z               (Swish, sigmoid(z) = 1 / (1 + exp(-z)))
+    u = s + b_add                    (external per-channel bias)
+    per row m and group g of C = N/G contiguous channels:
+        mu  = mean(u[m, gC:(g+1)C]),  var = population variance
+    y = (u - mu) / sqrt(var + eps) * gamma + beta
+
+All arithmetic is IEEE double in plain C (``lgn_oracle.c``), sequential sums,
+no FMA contraction.  Pins: ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lgn_oracle.c")
+_LIB = os.path.join(_HERE, "liblgn_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+# Portable flags: the library travels to other x86-64 hosts, so no -march=native.
+# -ffp-contract=off keeps every multiply and add separately rounded.
+_CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
+
+
+def build(force: bool = False) -> str:
+    """Compile ``liblgn_oracle.so`` with gcc (if missing or ``force``)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build()
+            lib = ctypes.CDLL(_LIB)
+            dp = ctypes.POINTER(ctypes.c_double)
+            L = ctypes.c_long
+            lib.oracle_swish.argtypes = [ctypes.c_double]
+            lib.oracle_swish.restype = ctypes.c_double
+            lib.oracle_swish_array.argtypes = [dp, dp, L]
+            lib.oracle_swish_array.restype = None
+            lib.oracle_linear.argtypes = [dp, dp, dp, L, L, L, dp]
+            lib.oracle_linear.restype = None
+            lib.oracle_groupnorm.argtypes = [dp, dp, dp, L, L, L, ctypes.c_double, dp, dp, dp]
+            lib.oracle_groupnorm.restype = None
+            lib.oracle_lgn_forward.argtypes = [dp, dp, dp, dp, dp, dp, L, L, L, L,
+                                               ctypes.c_double, dp]
+            lib.oracle_lgn_forward.restype = ctypes.c_int
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    """Widen to a C-contiguous float64 array (exact for fp32 / bf16 values)."""
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def swish(z) -> np.ndarray:
+    z = _f64(z)
+    out = np.empty_like(z)
+    _load().oracle_swish_array(_ptr(z), _ptr(out), z.size)
+    return out
+
+
+def swish_scalar(z: float) -> float:
+    return float(_load().oracle_swish(float(z)))
+
+
+def linear(x, W, b_lin) -> np.ndarray:
+    """z = x . W^T + b_lin  (x [M,K], W [N,K], b_lin [N])."""
+    x, W, b = _f64(x), _f64(W), _f64(b_lin)
+    M, K = x.shape
+    N, K2 = W.shape
+    assert K == K2 and b.shape == (N,)
+    z = np.empty((M, N), dtype=np.float64)
+    _load().oracle_linear(_ptr(x), _ptr(W), _ptr(b), M, K, N, _ptr(z))
+    return z
+
+
+def groupnorm(u, gamma, beta, G: int, eps: float, return_stats: bool = False):
+    """GroupNorm over contiguous channel groups of each row of u [M,N]."""
+    u, ga, be = _f64(u), _f64(gamma), _f64(beta)
+    M, N = u.shape
+    assert N % G == 0 and ga.shape == (N,) and be.shape == (N,)
+    y = np.empty((M, N), dtype=np.float64)
+    mean = np.empty((M, G), dtype=np.float64)
+    var = np.empty((M, G), dtype=np.float64)
+    _load().oracle_groupnorm(_ptr(u), _ptr(ga), _ptr(be), M, N, G, float(eps), _ptr(y),
+                             _ptr(mean), _ptr(var))
+    if return_stats:
+        return y, mean, var
+    return y
+
+
+def lgn_forward(x, W, b_lin, b_add, gamma, beta, G: int, eps: float) -> np.ndarray:
+    """The whole forward in fp64: y [M,N]."""
+    x, W = _f64(x), _f64(W)
+    b_lin, b_add, gamma, beta = _f64(b_lin), _f64(b_add), _f64(gamma), _f64(beta)
+    M, K = x.shape
+    N = W.shape[0]
+    assert W.shape == (N, K)
+    for v in (b_lin, b_add, gamma, beta):
+        assert v.shape == (N,)
+    y = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_lgn_forward(_ptr(x), _ptr(W), _ptr(b_lin), _ptr(b_add), _ptr(gamma),
+                                    _ptr(beta), M, K, N, G, float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_lgn_forward failed with code %d" % rc)
+    return y
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())

@@ -1,0 +1,163 @@
+/*
+ * lgn_oracle.c -- plain, slow, obviously correct CPU oracle for
+ *
+ *     y = GroupNorm_G( Swish(x . W^T + b_lin) + b_add ) * gamma + beta
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library and must never be called by
+ * the product path.
+ *
+ * Source of the definition: the POPCORNBENCH transcript "Kimi-K2.6 l2_p37"
+ * (Linear -> Swish -> add bias -> GroupNorm), its problem statement and the
+ * passages that spell out the forward order (linear with its own bias, then
+ * sigmoid(x)*x, then the external per-channel bias, then GroupNorm over
+ * contiguous channel groups with population variance and eps inside the
+ * square root, then the per-channel affine).
+ *
+ * Arithmetic: every value is an IEEE double; sums run in index order with no
+ * blocking, no reordering and no fused multiply-add (build with
+ * -ffp-contract=off).  Inputs given in fp32 or bf16 widen to double exactly.
+ * The only parallelism is independent output rows on OpenMP threads; it does
+ * not change any per-row arithmetic.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Linear layer, one row (P1 problem statement; weight stored as
+ * [out_features, in_features] like nn.Linear):
+ *   z[n] = sum_{k=0}^{K-1} x[k] * W[n][k] + b_lin[n]                       */
+static void linear_row(const double *xrow, const double *W, const double *b_lin,
+                       long K, long N, double *z)
+{
+    for (long n = 0; n < N; ++n) {
+        const double *wrow = W + (size_t)n * (size_t)K;
+        double s = 0.0;
+        for (long k = 0; k < K; ++k)
+            s += xrow[k] * wrow[k];
+        z[n] = s + b_lin[n];
+    }
+}
+
+/* Swish with unit slope, written as the page writes it: sigmoid(z) * z with
+ * sigmoid(z) = 1 / (1 + exp(-z)).                                           */
+double oracle_swish(double z)
+{
+    double sig = 1.0 / (1.0 + exp(-z));
+    return sig * z;
+}
+
+/* GroupNorm of one row of N channels split into G contiguous groups of
+ * C = N / G channels (P1: "channels for a group are contiguous").  Mean and
+ * population variance (divide by C) per group, eps added to the variance
+ * inside the square root, then per-channel gamma/beta.  Exact two-pass.
+ * mean_out / var_out, if non-NULL, receive the G per-group statistics.     */
+static void groupnorm_row(const double *u, const double *gamma, const double *beta,
+                          long N, long G, double eps, double *y,
+                          double *mean_out, double *var_out)
+{
+    long C = N / G;
+    for (long g = 0; g < G; ++g) {
+        const double *ug = u + g * C;
+        double s = 0.0;
+        for (long c = 0; c < C; ++c)
+            s += ug[c];
+        double mean = s / (double)C;
+        double ss = 0.0;
+        for (long c = 0; c < C; ++c) {
+            double d = ug[c] - mean;
+            ss += d * d;
+        }
+        double var = ss / (double)C;
+        double denom = sqrt(var + eps);
+        for (long c = 0; c < C; ++c) {
+            long n = g * C + c;
+            y[n] = (ug[c] - mean) / denom * gamma[n] + beta[n];
+        }
+        if (mean_out) mean_out[g] = mean;
+        if (var_out) var_out[g] = var;
+    }
+}
+
+/* ---- exported step functions (each step on its own, for pinning) ---- */
+
+/* z[M][N] = x[M][K] . W[N][K]^T + b_lin[N] */
+void oracle_linear(const double *x, const double *W, const double *b_lin,
+                   long M, long K, long N, double *z)
+{
+    long m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m)
+        linear_row(x + (size_t)m * (size_t)K, W, b_lin, K, N, z + (size_t)m * (size_t)N);
+}
+
+/* out[i] = swish(in[i]) for i < n */
+void oracle_swish_array(const double *in, double *out, long n)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = oracle_swish(in[i]);
+}
+
+/* y[M][N] = GroupNorm_G(u[M][N]) * gamma + beta; mean/var [M][G] optional */
+void oracle_groupnorm(const double *u, const double *gamma, const double *beta,
+                      long M, long N, long G, double eps, double *y,
+                      double *mean_out, double *var_out)
+{
+    long m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m)
+        groupnorm_row(u + (size_t)m * (size_t)N, gamma, beta, N, G, eps,
+                      y + (size_t)m * (size_t)N,
+                      mean_out ? mean_out + (size_t)m * (size_t)G : NULL,
+                      var_out ? var_out + (size_t)m * (size_t)G : NULL);
+}
+
+/* ---- the whole forward, row by row ----
+ * Returns 0 on success, -1 on bad arguments, -2 if a row buffer could not be
+ * allocated.                                                                 */
+int oracle_lgn_forward(const double *x, const double *W, const double *b_lin,
+                       const double *b_add, const double *gamma, const double *beta,
+                       long M, long K, long N, long G, double eps, double *y)
+{
+    if (M < 0 || K < 0 || N <= 0 || G <= 0 || N % G != 0)
+        return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *row = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!row) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        long m;
+#pragma omp for schedule(static)
+        for (m = 0; m < M; ++m) {
+            if (!row) continue;
+            double *yrow = y + (size_t)m * (size_t)N;
+            /* step 1: linear with its own bias */
+            linear_row(x + (size_t)m * (size_t)K, W, b_lin, K, N, row);
+            /* steps 2-3: swish, then the external per-channel bias */
+            for (long n = 0; n < N; ++n)
+                row[n] = oracle_swish(row[n]) + b_add[n];
+            /* steps 4-5: group statistics, normalise, affine */
+            groupnorm_row(row, gamma, beta, N, G, eps, yrow, NULL, NULL);
+        }
+        free(row);
+    }
+    return failed ? -2 : 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
