@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused Linear -> Swish -> +bias -> GroupNorm forward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--variant fused|twopass] [--no-cpu-baseline] [--no-extra]
+
+A step is one full forward (GEMM, bias, Swish, bias, GroupNorm statistics,
+normalise, affine, output write) over one batch of seeded synthetic input that
+is already resident in HBM.  W untimed warm-up steps, then K timed steps
+bracketed by torch.cuda.synchronize().  Prints ONE JSON line on stdout; a
+human-readable summary goes to stderr.
+
+value      : GEMM TFLOP/s of the whole timed region, 2*M*N*K*K_steps / wall time.
+roofline   : the fused kernel's own time per launch from HIP events recorded on
+             the launch stream around every timed launch, against the MI355X
+             dense MFMA peak of its input type (fp32 157.3, bf16 2500 TFLOP/s).
+             traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
+             counters (profiles/traffic.json), only if the kernel sources are
+             unchanged since the counters were taken, else null.
+cpu_baseline: the fp64 CPU oracle timed on the host on the first S rows of the
+             same workload (S sized to about --cpu-seconds of work).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused Linear+Swish+bias+GroupNorm TFLOP/s at M32768 K1024 N4096; % MFMA peak"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+DEFAULT_WORKLOAD = "m32768_k1024_n4096_g64_f32"
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "gemm_activation_groupnorm_amd", "csrc", "*")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(workload: str, variant: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get("%s/%s" % (workload, variant))
+    if not rec or rec.get("src_sha") != kernel_sources_sha():
+        return None
+    return rec.get("traffic_bytes")
+
+
+class Runner:
+    """Inputs resident on the GPU plus a launch() closure for one forward."""
+
+    def __init__(self, w, variant: str):
+        import numpy as np
+        import torch
+        from gemm_activation_groupnorm_amd import lgn
+        from gemm_activation_groupnorm_amd.inputs import workload_inputs
+
+        self.w, self.variant = w, variant
+        t0 = time.perf_counter()
+        self.inp = workload_inputs(w)
+        dev = "cuda:0"
+        self.d = {k: torch.from_numpy(np.ascontiguousarray(self.inp[k])).to(dev)
+                  for k in ("b_lin", "b_add", "gamma", "beta")}
+        if w.dtype == "bf16":
+            for k in ("x", "W"):
+                self.d[k] = torch.from_numpy(self.inp[k + "_bf16"].view(np.int16)).to(dev).view(
+                    torch.bfloat16)
+        else:
+            for k in ("x", "W"):
+                self.d[k] = torch.from_numpy(self.inp[k]).to(dev)
+        self.out = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        self.ws = None
+        if variant == "twopass":
+            self.ws = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        eprint("[bench] %s/%s inputs ready in %.1f s" % (w.name, variant, time.perf_counter() - t0))
+        self.stream = torch.cuda.current_stream()
+        d, out = self.d, self.out
+        args = (d["x"], d["W"], d["b_lin"], d["b_add"], d["gamma"], d["beta"],
+                w.M, w.K, w.N, w.G, w.eps, out)
+        s = self.stream
+        if variant == "fused":
+            fn = lgn.lgn_forward_f32 if w.dtype == "f32" else lgn.lgn_forward_bf16
+            self.launch = lambda: lgn.check(fn(*args, stream=s))
+        else:
+            fn = lgn.lgn_forward_twopass_f32 if w.dtype == "f32" else lgn.lgn_forward_twopass_bf16
+            nb = lgn.lgn_twopass_workspace_bytes(w.M, w.N)
+            ws = self.ws
+            self.launch = lambda: lgn.check(fn(*args, ws, nb, stream=s))
+
+    def time(self, steps: int, warmup: int):
+        import torch
+        for _ in range(warmup):
+            self.launch()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(self.stream)
+            self.launch()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kms = sorted(a.elapsed_time(b) for a, b in ev)
+        return wall, kms
+
+    def check_rows(self, nrows: int = 8):
+        import numpy as np
+        import oracle
+        from gemm_activation_groupnorm_amd.inputs import sample_rows
+        rows = sample_rows(self.w.M, nrows, seed=99)
+        import torch
+        idx = torch.from_numpy(rows).to(self.out.device)
+        y = self.out[idx].cpu().numpy().astype(np.float64)
+        i = self.inp
+        ref = oracle.lgn_forward(i["x"][rows], i["W"], i["b_lin"], i["b_add"], i["gamma"],
+                                 i["beta"], self.w.G, self.w.eps)
+        return float(np.max(np.abs(y - ref))), len(rows)
+
+
+def cpu_baseline(w, inp, seconds: float):
+    import oracle
+    x, W = inp["x"], inp["W"]
+    args = (inp["b_lin"], inp["b_add"], inp["gamma"], inp["beta"], w.G, w.eps)
+    probe = min(w.M, 32)
+    t0 = time.perf_counter()
+    oracle.lgn_forward(x[:probe], W, *args)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(max(probe, min(w.M, seconds / max(per_row, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.lgn_forward(x[:rows], W, *args)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "first %d of %d rows of %s, fp64 C oracle, %.1f s wall, %d OpenMP threads"
+                  % (rows, w.M, w.name, dt, oracle.num_threads()),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--variant", default="fused", choices=["fused", "twopass"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the secondary workloads (bf16, wide group, two-pass)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the forward shards over rows (or whole groups) "
+              "with no exchange, so a multi-GPU figure is N times the one-GPU figure on 1/N of "
+              "the rows and is not run here (--gpus %d, WORLD_SIZE %d)." % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gemm_activation_groupnorm_amd import build as hip_build
+    if not os.path.exists(hip_build.LIB):
+        hip_build.build()
+    from gemm_activation_groupnorm_amd.inputs import get_workload
+
+    w = get_workload(args.workload)
+    r = Runner(w, args.variant)
+    wall, kms = r.time(args.steps, args.warmup)
+    flops = float(w.flops)
+    ms_per_step = wall / args.steps * 1e3
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kmean = sum(kms) / len(kms)
+    achieved = flops / (kmean * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    err, nrows = r.check_rows()
+    eprint("[bench] %s/%s: %.3f ms/step, kernel mean %.3f ms (p10 %.3f, p90 %.3f) -> %.1f TFLOP/s "
+           "(%.1f%% of %.1f); sampled-row max err %.2e"
+           % (w.name, args.variant, ms_per_step, kmean, kms[len(kms) // 10],
+              kms[(len(kms) * 9) // 10], achieved, 100 * achieved / peak, peak, err))
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "G": w.G, "eps": w.eps,
+                   "seed": w.seed, "variant": args.variant,
+                   "inputs": "x~%g*N(0,1); W,b_lin~U(+-1/sqrt(K)); b_add~0.02*N(0,1); "
+                             "gamma~1+0.1*N(0,1); beta~0.1*N(0,1)" % w.x_scale},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_for(w.name, args.variant),
+            "kernel_ms_mean": round(kmean, 4),
+            "kernel": "lgn_fused_kernel" if args.variant == "fused" else "gemm+epilogue",
+        },
+        "check": {"rows": nrows, "max_abs_err_vs_oracle": err},
+    }
+    inp = r.inp
+    del r
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra = []
+        for name, variant in (("m32768_k1024_n4096_g64_bf16", "fused"),
+                              ("m16384_k2048_n8192_g8_f32", "fused"),
+                              (DEFAULT_WORKLOAD, "twopass")):
+            if name == w.name and variant == args.variant:
+                continue
+            we = get_workload(name)
+            re = Runner(we, variant)
+            wl, km = re.time(20, 5)
+            km_mean = sum(km) / len(km)
+            ach = we.flops / (km_mean * 1e-3) / 1e12
+            e2, _ = re.check_rows(4)
+            eprint("[bench] %s/%s: kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f), err %.2e"
+                   % (name, variant, km_mean, ach, 100 * ach / PEAK_TFLOPS[we.dtype],
+                      PEAK_TFLOPS[we.dtype], e2))
+            extra.append({"workload": name, "variant": variant, "dtype": we.dtype,
+                          "ms_per_step": round(wl / 20 * 1e3, 4), "kernel_ms_mean": round(km_mean, 4),
+                          "tflops": round(ach, 3), "frac_of_peak": round(ach / PEAK_TFLOPS[we.dtype], 4),
+                          "max_abs_err_vs_oracle": e2})
+            del re
+            torch.cuda.empty_cache()
+        res["extra"] = extra
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        eprint("[bench] cpu baseline: %s" % res["cpu_baseline"]["sample"])
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+// lgn_api.hip -- the C ABI of liblgn.so (declared in include/lgn.h):
+// argument validation (host only, before any HIP call), the gfx950 device
+// check, and dispatch to the kernel launchers.
+#include "../../include/lgn.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "lgn_launch.hpp"
+
+namespace {
+
+enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Sizes, eps and pointers.  Returns LGN_OK, LGN_ERR_INVALID_ARG or
+// LGN_ERR_UNSUPPORTED; makes no HIP call.
+lgn_status validate(int dtype, const void *x, const void *W, const float *b_lin,
+                    const float *b_add, const float *gamma, const float *beta, int M, int K, int N,
+                    int G, float eps, const float *out) {
+    if (M < 0 || K < 0 || N < 1 || G < 1) return LGN_ERR_INVALID_ARG;
+    if (N % G != 0) return LGN_ERR_INVALID_ARG;
+    if (!(eps > 0.0f) || !isfinite(eps)) return LGN_ERR_INVALID_ARG;
+    if (M == 0) return LGN_OK;   // empty batch: nothing is read or written
+    if (!b_lin || !b_add || !gamma || !beta || !out) return LGN_ERR_INVALID_ARG;
+    if (K > 0 && (!x || !W)) return LGN_ERR_INVALID_ARG;
+    const int epc = dtype == DT_F32 ? 4 : 8;   // elements per 16-byte load
+    if (K % epc != 0 || N % 4 != 0) return LGN_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(out, 16)) return LGN_ERR_UNSUPPORTED;
+    if (!aligned(b_lin, 4) || !aligned(b_add, 4) || !aligned(gamma, 4) || !aligned(beta, 4))
+        return LGN_ERR_UNSUPPORTED;
+    return LGN_OK;
+}
+
+// The HIP error behind the last LGN_ERR_HIP returned on this thread.
+thread_local hipError_t g_last_hip = hipSuccess;
+
+lgn_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return LGN_OK;
+    g_last_hip = e;
+    return LGN_ERR_HIP;
+}
+
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+lgn_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e);
+    if (dev < 0) return from_hip(hipErrorInvalidDevice);
+    if (dev < kMaxDevices) {
+        const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (c == 1) return LGN_OK;
+        if (c == 2) return LGN_ERR_UNSUPPORTED;
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return from_hip(e);
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? LGN_OK : LGN_ERR_UNSUPPORTED;
+}
+
+template <int DT, class T>
+lgn_status forward_fused(const T *x, const T *W, const float *b_lin, const float *b_add,
+                         const float *gamma, const float *beta, int M, int K, int N, int G,
+                         float eps, float *out, hipStream_t stream) {
+    lgn_status s = validate(DT, x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out);
+    if (s != LGN_OK || M == 0) return s;
+    if (!lgn::fused_cg_supported(N / G)) return LGN_ERR_UNSUPPORTED;
+    s = check_device();
+    if (s != LGN_OK) return s;
+    if (DT == DT_F32)
+        return from_hip(lgn::launch_fused_f32((const float *)x, (const float *)W, b_lin, b_add,
+                                              gamma, beta, M, K, N, G, eps, out, stream));
+    return from_hip(lgn::launch_fused_bf16((const uint16_t *)x, (const uint16_t *)W, b_lin,
+                                           b_add, gamma, beta, M, K, N, G, eps, out, stream));
+}
+
+template <int DT, class T>
+lgn_status forward_twopass(const T *x, const T *W, const float *b_lin, const float *b_add,
+                           const float *gamma, const float *beta, int M, int K, int N, int G,
+                           float eps, float *out, void *workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+    lgn_status s = validate(DT, x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out);
+    if (s != LGN_OK || M == 0) return s;
+    if (!workspace || ws_bytes < lgn_twopass_workspace_bytes(M, N)) return LGN_ERR_INVALID_ARG;
+    if (!aligned(workspace, 16)) return LGN_ERR_UNSUPPORTED;
+    s = check_device();
+    if (s != LGN_OK) return s;
+    float *z = (float *)workspace;
+    hipError_t e = DT == DT_F32
+                       ? lgn::launch_gemm_bias_f32((const float *)x, (const float *)W, b_lin, M,
+                                                   K, N, z, stream)
+                       : lgn::launch_gemm_bias_bf16((const uint16_t *)x, (const uint16_t *)W,
+                                                    b_lin, M, K, N, z, stream);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(lgn::launch_gn_epilogue(z, b_add, gamma, beta, M, N, G, eps, out, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+lgn_status lgn_forward_f32(const float *x, const float *W, const float *b_lin,
+                           const float *b_add, const float *gamma, const float *beta, int M,
+                           int K, int N, int G, float eps, float *out, hipStream_t stream) {
+    return forward_fused<DT_F32>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream);
+}
+
+lgn_status lgn_forward_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float *b_lin,
+                            const float *b_add, const float *gamma, const float *beta, int M,
+                            int K, int N, int G, float eps, float *out, hipStream_t stream) {
+    return forward_fused<DT_BF16>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream);
+}
+
+int lgn_fused_supported(int dtype, int M, int K, int N, int G) {
+    if (dtype != DT_F32 && dtype != DT_BF16) return 0;
+    if (M < 0 || K < 0 || N < 1 || G < 1 || N % G != 0) return 0;
+    const int epc = dtype == DT_F32 ? 4 : 8;
+    if (K % epc != 0 || N % 4 != 0) return 0;
+    return lgn::fused_cg_supported(N / G) ? 1 : 0;
+}
+
+size_t lgn_twopass_workspace_bytes(int M, int N) {
+    if (M <= 0 || N <= 0) return 0;
+    return (size_t)M * (size_t)N * sizeof(float);
+}
+
+lgn_status lgn_forward_twopass_f32(const float *x, const float *W, const float *b_lin,
+                                   const float *b_add, const float *gamma, const float *beta,
+                                   int M, int K, int N, int G, float eps, float *out,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return forward_twopass<DT_F32>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
+                                   workspace, workspace_bytes, stream);
+}
+
+lgn_status lgn_forward_twopass_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float *b_lin,
+                                    const float *b_add, const float *gamma, const float *beta,
+                                    int M, int K, int N, int G, float eps, float *out,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return forward_twopass<DT_BF16>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
+                                    workspace, workspace_bytes, stream);
+}
+
+const char *lgn_status_string(lgn_status s) {
+    switch (s) {
+        case LGN_OK: return "LGN_OK: success";
+        case LGN_ERR_INVALID_ARG:
+            return "LGN_ERR_INVALID_ARG: null pointer, bad size, N % G != 0, eps not > 0 and "
+                   "finite, or workspace too small";
+        case LGN_ERR_UNSUPPORTED:
+            return "LGN_ERR_UNSUPPORTED: device is not gfx950, or shape/alignment not covered "
+                   "(16-byte aligned x/W/out, N % 4 == 0, K % 4 (fp32) or K % 8 (bf16) == 0; "
+                   "fused: N/G a power of two in 8..1024)";
+        case LGN_ERR_HIP: return "LGN_ERR_HIP: a HIP runtime call or kernel launch failed";
+        default: return "unknown lgn_status";
+    }
+}
+
+const char *lgn_version(void) { return "0.1.0"; }
+
+const char *lgn_last_hip_error_string(void) {
+    return g_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip);
+}
+
+}  // extern "C"

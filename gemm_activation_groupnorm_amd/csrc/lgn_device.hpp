@@ -1,0 +1,246 @@
+// lgn_device.hpp -- device building blocks for gfx950 (CDNA4, wave64).
+//
+// The GEMM core computes the transposed tile  Z^T = W . x^T  with
+// v_mfma_f32_32x32x2_f32 (fp32 inputs) or v_mfma_f32_32x32x16_bf16 (bf16
+// inputs): the MFMA "A" operand is a 32-row slab of W (32 channels) and the
+// "B" operand a 32-row slab of x (32 samples).  In the 32x32 accumulator a
+// lane then holds ONE sample (lane % 32) and 16 channels,
+//     channel(r, h) = 8*(r/4) + 4*h + (r%4),   r = 0..15, h = lane / 32,
+// so a GroupNorm group of contiguous channels sits mostly inside one lane's
+// registers: the statistics need in-register sums, one exchange with lane^32
+// and, only for groups wider than a wave's channel span, one LDS merge.
+// Registers r = 4q..4q+3 are 4 contiguous channels -> one 16-byte store.
+//
+// Both operands are K-contiguous in memory (x is [M,K], W is [N,K], the
+// nn.Linear layout) and are staged through LDS in rows of ROWB bytes with a
+// 16-byte-chunk XOR swizzle, so that the 16 lanes of one LDS phase (16 rows,
+// same logical chunk) hit 16 distinct 16-byte bank groups of gfx950's
+// 64 x 4-byte banks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lgn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct f32_t {};   // tag: fp32 operands
+struct bf16_t {};  // tag: bf16 operands (raw uint16 storage)
+
+template <class DT> struct dt_traits;
+template <> struct dt_traits<f32_t> {
+    typedef float storage;
+    static constexpr int bytes = 4;
+};
+template <> struct dt_traits<bf16_t> {
+    typedef uint16_t storage;
+    static constexpr int bytes = 2;
+};
+
+// ---------------------------------------------------------------- tiles ----
+// BS samples x BC channels per workgroup; WAVES_S x WAVES_C waves; each wave
+// owns WS x WC = (32*TS) x (32*TC) of the tile.  ROWB bytes of K per LDS row.
+template <class DT, int BS_, int BC_, int WAVES_S_, int WAVES_C_, int ROWB_>
+struct TileCfg {
+    static constexpr int BS = BS_, BC = BC_, WAVES_S = WAVES_S_, WAVES_C = WAVES_C_;
+    static constexpr int ROWB = ROWB_;
+    static constexpr int NT = 64 * WAVES_S * WAVES_C;
+    static constexpr int WS = BS / WAVES_S, WC = BC / WAVES_C;
+    static constexpr int TS = WS / 32, TC = WC / 32;
+    static constexpr int EB = dt_traits<DT>::bytes;
+    static constexpr int EPC = 16 / EB;               // elements per 16-byte chunk
+    static constexpr int CPR = ROWB / 16;             // chunks per LDS row
+    static constexpr int BK = CPR * EPC;              // K elements per stage
+    static constexpr int ROWS = BS + BC;              // W rows first, then x rows
+    static constexpr int CHUNKS = ROWS * CPR;
+    static constexpr int CPT = (CHUNKS + NT - 1) / NT;
+    static constexpr int STAGE_BYTES = ROWS * ROWB;
+    static constexpr int RPW = 256 / ROWB;            // rows per 256-byte bank window
+    static_assert(WS % 32 == 0 && WC % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
+    static_assert(ROWB == 32 || ROWB == 64 || ROWB == 128, "LDS row of 32, 64 or 128 bytes");
+    static_assert(NT % CPR == 0, "every thread keeps one chunk column");
+    static_assert((BC * CPR) % NT == 0 || CHUNKS % NT == 0 || true, "");
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row r.
+template <class Cfg>
+__device__ __forceinline__ int swz(int r, int c) {
+    return c ^ ((r / Cfg::RPW) % Cfg::CPR);
+}
+
+// --------------------------------------------------------------- MFMA ----
+template <class DT> struct Mfma;
+
+template <> struct Mfma<f32_t> {
+    // One 16-byte fragment per operand = 4 K-steps of v_mfma_f32_32x32x2_f32.
+    // Lane half h feeds K slot h of each step with the k = 4h + kk element of
+    // the 8-wide K chunk; A and B use the same assignment, so the pair of
+    // steps kk covers the chunk exactly once.
+    static __device__ __forceinline__ void run(f32x16 &acc, u32x4 a, u32x4 b) {
+        f32x4 af = __builtin_bit_cast(f32x4, a);
+        f32x4 bf = __builtin_bit_cast(f32x4, b);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[0], bf[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[1], bf[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2], bf[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[3], bf[3], acc, 0, 0, 0);
+    }
+};
+
+template <> struct Mfma<bf16_t> {
+    // One 16-byte fragment = 8 bf16 = the lane's K slice of one
+    // v_mfma_f32_32x32x16_bf16.
+    static __device__ __forceinline__ void run(f32x16 &acc, u32x4 a, u32x4 b) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+};
+
+// ----------------------------------------------------------- GEMM core ----
+// Accumulates acc[ts][tc] (32 samples x 32 channels each) for the workgroup
+// tile at (m0, n0) over the whole K range.  Global -> register prefetch of the
+// next stage overlaps the MFMAs of the current one; two LDS stages, one
+// barrier per stage.  Rows past M or N and K past the end load as zeros.
+template <class DT, class Cfg>
+struct GemmCore {
+    typedef typename dt_traits<DT>::storage T;
+
+    static __device__ __forceinline__ void load_global(const T *__restrict__ x,
+                                                       const T *__restrict__ W, int M, int N,
+                                                       int K, int m0, int n0, int k0, int tid,
+                                                       u32x4 (&pref)[Cfg::CPT]) {
+#pragma unroll
+        for (int i = 0; i < Cfg::CPT; ++i) {
+            const int idx = tid + i * Cfg::NT;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (Cfg::CHUNKS % Cfg::NT == 0 || idx < Cfg::CHUNKS) {
+                const int r = idx / Cfg::CPR;
+                const int c = idx % Cfg::CPR;
+                const int k = k0 + c * Cfg::EPC;
+                if (r < Cfg::BC) {
+                    const int n = n0 + r;
+                    if (n < N && k < K)
+                        v = *reinterpret_cast<const u32x4 *>(W + (size_t)n * (size_t)K + k);
+                } else {
+                    const int m = m0 + (r - Cfg::BC);
+                    if (m < M && k < K)
+                        v = *reinterpret_cast<const u32x4 *>(x + (size_t)m * (size_t)K + k);
+                }
+            }
+            pref[i] = v;
+        }
+    }
+
+    static __device__ __forceinline__ void store_lds(unsigned char *stage, int tid,
+                                                     const u32x4 (&pref)[Cfg::CPT]) {
+#pragma unroll
+        for (int i = 0; i < Cfg::CPT; ++i) {
+            const int idx = tid + i * Cfg::NT;
+            if (Cfg::CHUNKS % Cfg::NT == 0 || idx < Cfg::CHUNKS) {
+                const int r = idx / Cfg::CPR;
+                const int c = idx % Cfg::CPR;
+                *reinterpret_cast<u32x4 *>(stage + r * Cfg::ROWB + 16 * swz<Cfg>(r, c)) = pref[i];
+            }
+        }
+    }
+
+    // wc0 / ws0: first channel / sample of this wave inside the tile.
+    static __device__ __forceinline__ void compute_stage(const unsigned char *stage, int wc0,
+                                                         int ws0, int lr, int h,
+                                                         f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+#pragma unroll
+        for (int cp = 0; cp < Cfg::CPR / 2; ++cp) {
+            const int c = 2 * cp + h;
+            u32x4 a[Cfg::TC], b[Cfg::TS];
+#pragma unroll
+            for (int tc = 0; tc < Cfg::TC; ++tc) {
+                const int r = wc0 + 32 * tc + lr;
+                a[tc] = *reinterpret_cast<const u32x4 *>(stage + r * Cfg::ROWB + 16 * swz<Cfg>(r, c));
+            }
+#pragma unroll
+            for (int ts = 0; ts < Cfg::TS; ++ts) {
+                const int r = Cfg::BC + ws0 + 32 * ts + lr;
+                b[ts] = *reinterpret_cast<const u32x4 *>(stage + r * Cfg::ROWB + 16 * swz<Cfg>(r, c));
+            }
+#pragma unroll
+            for (int ts = 0; ts < Cfg::TS; ++ts)
+#pragma unroll
+                for (int tc = 0; tc < Cfg::TC; ++tc)
+                    Mfma<DT>::run(acc[ts][tc], a[tc], b[ts]);
+        }
+    }
+
+    static __device__ __forceinline__ void run(const T *__restrict__ x, const T *__restrict__ W,
+                                               int M, int N, int K, int m0, int n0,
+                                               unsigned char *smem, int tid, int wc0, int ws0,
+                                               int lr, int h, f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+#pragma unroll
+        for (int ts = 0; ts < Cfg::TS; ++ts)
+#pragma unroll
+            for (int tc = 0; tc < Cfg::TC; ++tc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[ts][tc][r] = 0.0f;
+
+        const int KT = (K + Cfg::BK - 1) / Cfg::BK;
+        if (KT == 0) return;
+        u32x4 pref[Cfg::CPT];
+        load_global(x, W, M, N, K, m0, n0, 0, tid, pref);
+        store_lds(smem, tid, pref);
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            unsigned char *cur = smem + (kt & 1) * Cfg::STAGE_BYTES;
+            unsigned char *nxt = smem + ((kt + 1) & 1) * Cfg::STAGE_BYTES;
+            const bool more = kt + 1 < KT;
+            if (more) load_global(x, W, M, N, K, m0, n0, (kt + 1) * Cfg::BK, tid, pref);
+            compute_stage(cur, wc0, ws0, lr, h, acc);
+            if (more) store_lds(nxt, tid, pref);
+            __syncthreads();
+        }
+    }
+};
+
+// ------------------------------------------------------ tile schedule ----
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Remap the hardware id so that each XCD receives a contiguous run of
+// logical tiles, then walk tiles in column-major order inside bands of
+// GROUP_M sample-tiles, so that the workgroups resident on one XCD at the
+// same time share x rows and W rows through that XCD's L2.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n,
+                                            int &tm, int &tn) {
+    int t = bid;
+    if ((nblocks & 7) == 0) t = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+    const int per_band = GROUP_M * tiles_n;
+    const int band = t / per_band;
+    const int first_m = band * GROUP_M;
+    const int rem = tiles_m - first_m;
+    const int gsize = rem < GROUP_M ? rem : GROUP_M;
+    const int local = t - band * per_band;
+    tm = first_m + local % gsize;
+    tn = local / gsize;
+}
+
+// ------------------------------------------------------- elementwise ----
+// Swish with unit slope: v * sigmoid(v), sigmoid(v) = 1 / (1 + e^-v), with
+// e^-v = 2^(-v*log2 e) on the hardware exp2 and a hardware reciprocal.  For
+// v -> -inf, e^-v -> +inf and the reciprocal -> 0, so the result -> -0.
+__device__ __forceinline__ float swish(float v) {
+    const float e = __builtin_amdgcn_exp2f(v * -1.4426950408889634f);
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Merge of two equal-count partial statistics (count n each) held by this
+// lane and by lane^32.  Written symmetrically so that both lanes obtain
+// bitwise identical results.
+__device__ __forceinline__ void merge_halves(float &mean, float &m2, float n) {
+    const float om = __shfl_xor(mean, 32);
+    const float om2 = __shfl_xor(m2, 32);
+    const float d = mean - om;
+    mean = (mean + om) * 0.5f;
+    m2 = (m2 + om2) + d * d * (0.5f * n);
+}
+
+}  // namespace lgn

@@ -1,0 +1,50 @@
+// lgn_launch.hpp -- host-side launchers of the kernel instantiations.  Each
+// returns the HIP error of the launch; argument validation has been done by
+// the caller (lgn_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+
+namespace lgn {
+
+// Launches `kernel` with hipLaunchKernel and returns that call's own status
+// (not a sticky error left by some earlier runtime call).  Arguments are
+// converted to the kernel's parameter types first.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                         Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    std::tuple<KArgs...> packed(args...);
+    void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    std::apply([&](auto &...e) {
+        int i = 0;
+        ((argv[i++] = (void *)&e), ...);
+    }, packed);
+    return hipLaunchKernel((const void *)kernel, grid, block, argv, 0, stream);
+}
+
+// Channel-per-group counts the fused kernel is instantiated for.
+inline bool fused_cg_supported(int cg) {
+    return cg == 8 || cg == 16 || cg == 32 || cg == 64 || cg == 128 || cg == 256 ||
+           cg == 512 || cg == 1024;
+}
+
+hipError_t launch_fused_f32(const float *x, const float *W, const float *b_lin,
+                            const float *b_add, const float *gamma, const float *beta, int M,
+                            int K, int N, int G, float eps, float *out, hipStream_t stream);
+hipError_t launch_fused_bf16(const uint16_t *x, const uint16_t *W, const float *b_lin,
+                             const float *b_add, const float *gamma, const float *beta, int M,
+                             int K, int N, int G, float eps, float *out, hipStream_t stream);
+
+hipError_t launch_gemm_bias_f32(const float *x, const float *W, const float *b_lin, int M,
+                                int K, int N, float *z, hipStream_t stream);
+hipError_t launch_gemm_bias_bf16(const uint16_t *x, const uint16_t *W, const float *b_lin,
+                                 int M, int K, int N, float *z, hipStream_t stream);
+hipError_t launch_gn_epilogue(const float *z, const float *b_add, const float *gamma,
+                              const float *beta, int M, int N, int G, float eps, float *out,
+                              hipStream_t stream);
+
+}  // namespace lgn

@@ -1,0 +1,67 @@
+// Two-pass ablation: GEMM + linear bias into a workspace, then the
+// elementwise + GroupNorm epilogue.
+#include "lgn_launch.hpp"
+#include "lgn_twopass.hpp"
+
+namespace lgn {
+
+template <class DT>
+static hipError_t launch_gemm_bias(const typename dt_traits<DT>::storage *x,
+                                   const typename dt_traits<DT>::storage *W, const float *b_lin,
+                                   int M, int K, int N, float *z, hipStream_t stream) {
+    typedef TileCfg<DT, 128, 128, 2, 2, 128> Cfg;
+    const int tiles_m = (M + Cfg::BS - 1) / Cfg::BS;
+    const int tiles_n = (N + Cfg::BC - 1) / Cfg::BC;
+    const long long blocks = (long long)tiles_m * tiles_n;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    return launch_kernel(lgn_gemm_bias_kernel<DT, Cfg>, dim3((unsigned)blocks), dim3(Cfg::NT),
+                         stream, x, W, b_lin, M, K, N, z, tiles_m, tiles_n);
+}
+
+hipError_t launch_gemm_bias_f32(const float *x, const float *W, const float *b_lin, int M,
+                                int K, int N, float *z, hipStream_t stream) {
+    return launch_gemm_bias<f32_t>(x, W, b_lin, M, K, N, z, stream);
+}
+
+hipError_t launch_gemm_bias_bf16(const uint16_t *x, const uint16_t *W, const float *b_lin,
+                                 int M, int K, int N, float *z, hipStream_t stream) {
+    return launch_gemm_bias<bf16_t>(x, W, b_lin, M, K, N, z, stream);
+}
+
+template <int LPG, int V>
+static hipError_t launch_vec(const float *z, const float *b_add, const float *gamma,
+                             const float *beta, long long pairs, int G, float eps, float *out,
+                             hipStream_t stream) {
+    constexpr long long per_block = 4 * (64 / LPG);
+    const long long blocks = (pairs + per_block - 1) / per_block;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    return launch_kernel(lgn_gn_epilogue_vec_kernel<LPG, V>, dim3((unsigned)blocks), dim3(256),
+                         stream, z, b_add, gamma, beta, pairs, G, eps, out);
+}
+
+hipError_t launch_gn_epilogue(const float *z, const float *b_add, const float *gamma,
+                              const float *beta, int M, int N, int G, float eps, float *out,
+                              hipStream_t stream) {
+    const int cg = N / G;
+    const long long pairs = (long long)M * G;
+    switch (cg) {
+        case 4: return launch_vec<1, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 8: return launch_vec<2, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 16: return launch_vec<4, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 32: return launch_vec<8, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 64: return launch_vec<16, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 128: return launch_vec<32, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 256: return launch_vec<64, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 512: return launch_vec<64, 2>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 1024: return launch_vec<64, 4>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        default: {
+            const long long blocks = (pairs + 3) / 4;
+            if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+            return launch_kernel(lgn_gn_epilogue_generic_kernel, dim3((unsigned)blocks),
+                                 dim3(256), stream, z, b_add, gamma, beta, pairs, G, cg, eps,
+                                 out);
+        }
+    }
+}
+
+}  // namespace lgn

@@ -1,0 +1,158 @@
+// lgn_twopass.hpp -- the two-pass ablation: kernel 1 is the MFMA GEMM with
+// the linear bias, writing z to a workspace; kernel 2 is one elementwise +
+// GroupNorm pass over z.  This is the structure the transcript settles on
+// (a library GEMM, then a fused Swish/bias/GroupNorm tail kernel working on
+// the GEMM output in place), rebuilt for gfx950.
+#pragma once
+
+#include "lgn_device.hpp"
+
+namespace lgn {
+
+// z[m, n] = sum_k x[m,k] W[n,k] + b_lin[n], fp32, [M, N] row-major.
+template <class DT, class Cfg>
+__global__ __launch_bounds__(Cfg::NT) void lgn_gemm_bias_kernel(
+    const typename dt_traits<DT>::storage *__restrict__ x,
+    const typename dt_traits<DT>::storage *__restrict__ W, const float *__restrict__ b_lin,
+    int M, int K, int N, float *__restrict__ z, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * Cfg::STAGE_BYTES];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 31;
+    const int h = lane >> 5;
+    const int ws0 = (wave / Cfg::WAVES_C) * Cfg::WS;
+    const int wc0 = (wave % Cfg::WAVES_C) * Cfg::WC;
+    int tm, tn;
+    tile_coords<8>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * Cfg::BS;
+    const int n0 = tn * Cfg::BC;
+
+    f32x16 acc[Cfg::TS][Cfg::TC];
+    GemmCore<DT, Cfg>::run(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
+
+#pragma unroll
+    for (int tc = 0; tc < Cfg::TC; ++tc) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = n0 + wc0 + 32 * tc + 8 * q + 4 * h;
+            if (c >= N) continue;
+            float bl[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bl[j] = b_lin[c + j];
+#pragma unroll
+            for (int ts = 0; ts < Cfg::TS; ++ts) {
+                const int m = m0 + ws0 + 32 * ts + lr;
+                if (m >= M) continue;
+                f32x4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = acc[ts][tc][4 * q + j] + bl[j];
+                *reinterpret_cast<f32x4 *>(z + (size_t)m * (size_t)N + c) = v;
+            }
+        }
+    }
+}
+
+// Epilogue, vectorised: a group of CG = 4*LPG*V channels is handled by LPG
+// lanes holding V float4 chunks each; one wave covers 64/LPG consecutive
+// (row, group) pairs, i.e. 256*V contiguous floats.  (row, group) pair p
+// starts at float p*CG because groups are contiguous inside a row.
+// Statistics: per-lane local two-pass, then an xor-butterfly of equal-count
+// Chan merges inside each LPG-lane segment.  In place (out == z) is safe:
+// every value is read before the pair's outputs are written, by the same
+// lane.
+template <int LPG, int V>
+__global__ __launch_bounds__(256) void lgn_gn_epilogue_vec_kernel(
+    const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
+    const float *__restrict__ beta, long long pairs, int G, float eps, float *out) {
+    constexpr int CG = 4 * LPG * V;
+    constexpr int PPW = 64 / LPG;   // pairs per wave
+    const int lane = threadIdx.x & 63;
+    const long long wave_global = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long p = wave_global * PPW + lane / LPG;
+    const int j = lane % LPG;
+    const bool live = p < pairs;
+    const int g = live ? (int)(p % G) : 0;
+    const size_t base = (size_t)(live ? p : 0) * CG;
+
+    f32x4 u[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int cc = 4 * (j + LPG * v);
+        f32x4 val = {0.f, 0.f, 0.f, 0.f};
+        if (live) {
+            val = *reinterpret_cast<const f32x4 *>(z + base + cc);
+            const int ch = g * CG + cc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] = swish(val[e]) + b_add[ch + e];
+        }
+        u[v] = val;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum += u[v][e];
+    float mean = sum * (1.0f / (4 * V));
+    float m2 = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float d = u[v][e] - mean;
+            m2 += d * d;
+        }
+    float n = (float)(4 * V);
+#pragma unroll
+    for (int off = 1; off < LPG; off <<= 1) {
+        const float om = __shfl_xor(mean, off);
+        const float om2 = __shfl_xor(m2, off);
+        const float d = mean - om;
+        mean = (mean + om) * 0.5f;
+        m2 = (m2 + om2) + d * d * (0.5f * n);
+        n *= 2.0f;
+    }
+    const float rstd = __builtin_amdgcn_rsqf(m2 * (1.0f / CG) + eps);
+    if (!live) return;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int cc = 4 * (j + LPG * v);
+        const int ch = g * CG + cc;
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (u[v][e] - mean) * rstd * gamma[ch + e] + beta[ch + e];
+        *reinterpret_cast<f32x4 *>(out + base + cc) = y;
+    }
+}
+
+// Epilogue, any channel count: one wave per (row, group), three passes over
+// the group (sum; sum of squared deviations from the mean; normalise), each
+// an xor-butterfly sum over the wave.  Used when C is not 4*LPG*V.
+__global__ __launch_bounds__(256) void lgn_gn_epilogue_generic_kernel(
+    const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
+    const float *__restrict__ beta, long long pairs, int G, int CG, float eps, float *out) {
+    const int lane = threadIdx.x & 63;
+    const long long p = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p >= pairs) return;   // whole wave leaves together
+    const int g = (int)(p % G);
+    const size_t base = (size_t)p * CG;
+    float sum = 0.f;
+    for (int c = lane; c < CG; c += 64) sum += swish(z[base + c]) + b_add[g * CG + c];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
+    const float mean = sum / (float)CG;
+    float ss = 0.f;
+    for (int c = lane; c < CG; c += 64) {
+        const float d = swish(z[base + c]) + b_add[g * CG + c] - mean;
+        ss += d * d;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+    const float rstd = __builtin_amdgcn_rsqf(ss / (float)CG + eps);
+    for (int c = lane; c < CG; c += 64) {
+        const float uu = swish(z[base + c]) + b_add[g * CG + c];
+        out[base + c] = (uu - mean) * rstd * gamma[g * CG + c] + beta[g * CG + c];
+    }
+}
+
+}  // namespace lgn

@@ -1,0 +1,167 @@
+"""ctypes binding of liblgn.so, entry point for entry point (include/lgn.h).
+
+Argument marshalling only: every array argument may be a torch tensor on the
+GPU (dense, of the dtype the C signature names) or a raw device address
+(int); ``stream`` may be a ``torch.cuda.Stream``, a raw ``hipStream_t``
+(int) or ``None`` for torch's current stream.  Each call returns the C
+status code unchanged; ``check(status)`` turns a non-zero code into
+``LgnError``.  Nothing here computes: the forward runs in liblgn.so's HIP
+kernels, and importing this module fails loudly if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblgn.so")
+
+LGN_OK = 0
+LGN_ERR_INVALID_ARG = 1
+LGN_ERR_UNSUPPORTED = 2
+LGN_ERR_HIP = 3
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+# Every symbol include/lgn.h declares.
+EXPORTS = (
+    "lgn_forward_f32",
+    "lgn_forward_bf16",
+    "lgn_fused_supported",
+    "lgn_twopass_workspace_bytes",
+    "lgn_forward_twopass_f32",
+    "lgn_forward_twopass_bf16",
+    "lgn_status_string",
+    "lgn_version",
+    "lgn_last_hip_error_string",
+)
+
+
+class LgnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = "lgn status %d: %s" % (status, lgn_status_string(status))
+        if status == LGN_ERR_HIP:
+            msg += " (%s)" % lgn_last_hip_error_string()
+        super().__init__(msg)
+
+
+def _load():
+    # PyTorch ships its own HIP runtime under the same SONAME
+    # (libamdhip64.so.7).  Loading torch first makes liblgn.so bind to that
+    # already-loaded runtime, so the process has ONE HIP runtime and torch's
+    # streams and allocations are valid handles for the library.  Loaded the
+    # other way round, two runtimes would coexist and the second one may not
+    # see the device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("liblgn.so not built at %s; run "
+                          "`python -m gemm_activation_groupnorm_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    fwd = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, vp]
+    two = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, vp, sz, vp]
+    for name, args, res in (
+        ("lgn_forward_f32", fwd, i),
+        ("lgn_forward_bf16", fwd, i),
+        ("lgn_fused_supported", [i, i, i, i, i], i),
+        ("lgn_twopass_workspace_bytes", [i, i], sz),
+        ("lgn_forward_twopass_f32", two, i),
+        ("lgn_forward_twopass_bf16", two, i),
+        ("lgn_status_string", [i], ctypes.c_char_p),
+        ("lgn_version", [], ctypes.c_char_p),
+        ("lgn_last_hip_error_string", [], ctypes.c_char_p),
+    ):
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def _ptr(a, want: Optional[str]) -> Optional[int]:
+    """Device address of a tensor (checked dense and of dtype ``want``) or int."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    import torch
+    if not isinstance(a, torch.Tensor):
+        raise TypeError("expected a torch.Tensor or an int address, got %r" % type(a))
+    if not a.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous (dense row-major)")
+    if want == "f32" and a.dtype != torch.float32:
+        raise ValueError("expected float32, got %s" % a.dtype)
+    if want == "bf16" and a.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("expected bfloat16 (or 16-bit raw bits), got %s" % a.dtype)
+    return a.data_ptr() if a.numel() > 0 else None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def lgn_forward_f32(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream=None) -> int:
+    return _lib.lgn_forward_f32(_ptr(x, "f32"), _ptr(W, "f32"), _ptr(b_lin, "f32"),
+                                _ptr(b_add, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
+                                M, K, N, G, eps, _ptr(out, "f32"), _stream(stream))
+
+
+def lgn_forward_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream=None) -> int:
+    return _lib.lgn_forward_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b_lin, "f32"),
+                                 _ptr(b_add, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
+                                 M, K, N, G, eps, _ptr(out, "f32"), _stream(stream))
+
+
+def lgn_fused_supported(dtype: int, M: int, K: int, N: int, G: int) -> int:
+    return _lib.lgn_fused_supported(dtype, M, K, N, G)
+
+
+def lgn_twopass_workspace_bytes(M: int, N: int) -> int:
+    return _lib.lgn_twopass_workspace_bytes(M, N)
+
+
+def lgn_forward_twopass_f32(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
+                            workspace, workspace_bytes, stream=None) -> int:
+    return _lib.lgn_forward_twopass_f32(_ptr(x, "f32"), _ptr(W, "f32"), _ptr(b_lin, "f32"),
+                                        _ptr(b_add, "f32"), _ptr(gamma, "f32"),
+                                        _ptr(beta, "f32"), M, K, N, G, eps, _ptr(out, "f32"),
+                                        _ptr(workspace, None), workspace_bytes, _stream(stream))
+
+
+def lgn_forward_twopass_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
+                             workspace, workspace_bytes, stream=None) -> int:
+    return _lib.lgn_forward_twopass_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b_lin, "f32"),
+                                         _ptr(b_add, "f32"), _ptr(gamma, "f32"),
+                                         _ptr(beta, "f32"), M, K, N, G, eps, _ptr(out, "f32"),
+                                         _ptr(workspace, None), workspace_bytes,
+                                         _stream(stream))
+
+
+def lgn_status_string(status: int) -> str:
+    return _lib.lgn_status_string(status).decode()
+
+
+def lgn_version() -> str:
+    return _lib.lgn_version().decode()
+
+
+def lgn_last_hip_error_string() -> str:
+    return _lib.lgn_last_hip_error_string().decode()
+
+
+def check(status: int) -> None:
+    if status != LGN_OK:
+        raise LgnError(status)

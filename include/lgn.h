@@ -1,0 +1,127 @@
+/*
+ * lgn.h -- C ABI of liblgn.so: fused Linear -> Swish -> +bias -> GroupNorm
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (POPCORNBENCH transcript "Kimi-K2.6 l2_p37", problem
+ * statement and the passages fixing the forward order):
+ *
+ *   z[m,n] = sum_k x[m,k] * W[n,k] + b_lin[n]        nn.Linear, W is [N,K]
+ *   u[m,n] = z[m,n] * sigmoid(z[m,n]) + b_add[n]      Swish, then the bias
+ *   for each row m and group g of C = N/G contiguous channels:
+ *       mu  = mean of u[m, gC .. gC+C-1]
+ *       var = population variance (divide by C) of the same values
+ *   y[m,n] = (u[m,n] - mu) / sqrt(var + eps) * gamma[n] + beta[n]
+ *
+ * Layouts: x [M,K], W [N,K], out [M,N], all dense row-major with no stride
+ * arguments; b_lin, b_add, gamma, beta are [N] fp32; out is always fp32.
+ *
+ * Ownership: every pointer is DEVICE memory owned by the caller, on the
+ * device that is current when the call is made.  The library allocates and
+ * frees nothing.  `out` must not overlap any input.  The two-pass workspace
+ * may be the same buffer as `out` (it is then overwritten in place) but must
+ * not overlap any input.
+ *
+ * Execution: every call enqueues its kernels on `stream` and returns without
+ * waiting; results are visible after the caller synchronises the stream.
+ * Calls keep no state between them except a per-device cache of the device
+ * architecture, so concurrent calls on different streams are safe.  Output is
+ * bitwise reproducible run to run (fixed reduction order, no atomics).
+ *
+ * Errors: calls return an lgn_status.  Argument errors are detected before any
+ * HIP call and nothing is launched.  Faults inside a kernel surface at the
+ * caller's synchronisation, as for any HIP kernel.
+ */
+#ifndef LGN_H
+#define LGN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int lgn_status;
+enum {
+    LGN_OK = 0,
+    LGN_ERR_INVALID_ARG = 1, /* null pointer, bad size, N % G != 0, eps not > 0 and finite,
+                                workspace too small */
+    LGN_ERR_UNSUPPORTED = 2, /* device is not gfx950, or a shape/alignment outside what the
+                                kernels cover (see each entry point) */
+    LGN_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+};
+
+/* Raw bfloat16 bits: the upper 16 bits of an IEEE binary32. */
+typedef uint16_t lgn_bf16;
+
+/* Shape rules common to every entry point:
+ *   M >= 0 (M == 0 launches nothing and returns LGN_OK), K >= 0, N >= 1,
+ *   G >= 1, N % G == 0, eps > 0 and finite.
+ *   Pointers may be NULL only when the array they address is empty
+ *   (x when M*K == 0, W when K == 0).
+ *   128-bit paths: x, W and out must be 16-byte aligned, N % 4 == 0, and
+ *   K % 4 == 0 (fp32 inputs) or K % 8 == 0 (bf16 inputs); otherwise
+ *   LGN_ERR_UNSUPPORTED.  b_lin, b_add, gamma, beta need 4-byte alignment. */
+
+/* Fused single-kernel forward, fp32 x and W, fp32 MFMA with fp32 accumulate.
+ * One kernel: MFMA GEMM tile, then bias, Swish, bias, group statistics,
+ * normalisation and affine in registers, and one write of `out`.
+ * Covers channel-per-group counts C = N/G that are powers of two from 8 to
+ * 1024; other C return LGN_ERR_UNSUPPORTED (the two-pass entry point covers
+ * every C). */
+lgn_status lgn_forward_f32(const float *x, const float *W,
+                           const float *b_lin, const float *b_add,
+                           const float *gamma, const float *beta,
+                           int M, int K, int N, int G, float eps,
+                           float *out, hipStream_t stream);
+
+/* Same as lgn_forward_f32 with x and W in bfloat16 (bf16 MFMA, fp32
+ * accumulate); biases, gamma, beta and out stay fp32. */
+lgn_status lgn_forward_bf16(const lgn_bf16 *x, const lgn_bf16 *W,
+                            const float *b_lin, const float *b_add,
+                            const float *gamma, const float *beta,
+                            int M, int K, int N, int G, float eps,
+                            float *out, hipStream_t stream);
+
+/* Whether the fused entry point covers this shape (1) or not (0), for dtype
+ * 0 = fp32 inputs, 1 = bf16 inputs.  Pure host logic; no HIP call. */
+int lgn_fused_supported(int dtype, int M, int K, int N, int G);
+
+/* Two-pass ablation (the transcript's adopted design: GEMM, then one fused
+ * elementwise + GroupNorm kernel).  Kernel 1 writes z = x.W^T + b_lin as fp32
+ * [M,N] into `workspace`; kernel 2 reads z, applies Swish, b_add, the group
+ * statistics and the affine, and writes `out`.  `workspace` must hold
+ * lgn_twopass_workspace_bytes(M, N) bytes, be 16-byte aligned, and may be the
+ * same pointer as `out`.  Covers every C = N/G. */
+size_t lgn_twopass_workspace_bytes(int M, int N);
+
+lgn_status lgn_forward_twopass_f32(const float *x, const float *W,
+                                   const float *b_lin, const float *b_add,
+                                   const float *gamma, const float *beta,
+                                   int M, int K, int N, int G, float eps,
+                                   float *out, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+lgn_status lgn_forward_twopass_bf16(const lgn_bf16 *x, const lgn_bf16 *W,
+                                    const float *b_lin, const float *b_add,
+                                    const float *gamma, const float *beta,
+                                    int M, int K, int N, int G, float eps,
+                                    float *out, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *lgn_status_string(lgn_status s);
+
+/* Library version as "major.minor.patch". */
+const char *lgn_version(void);
+
+/* Text of the HIP error behind the last LGN_ERR_HIP returned on the calling
+ * thread ("no HIP error" if none).  Static storage; do not free. */
+const char *lgn_last_hip_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LGN_H */

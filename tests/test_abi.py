@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/lgn.h declares, and rejects bad arguments before any HIP call."""
+import math
+import os
+import re
+
+import pytest
+
+from gemm_activation_groupnorm_amd import lgn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 1 << 20          # a 16-byte aligned fake device address; never dereferenced
+GOOD = dict(M=64, K=32, N=128, G=8, eps=1e-5)
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "lgn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lgn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(lgn.EXPORTS)
+
+
+@pytest.mark.parametrize("name", declared_symbols())
+def test_library_exports_symbol(name):
+    assert hasattr(lgn._lib, name)
+
+
+def test_status_strings_and_version():
+    for s in (lgn.LGN_OK, lgn.LGN_ERR_INVALID_ARG, lgn.LGN_ERR_UNSUPPORTED, lgn.LGN_ERR_HIP):
+        assert lgn.lgn_status_string(s).startswith(
+            ["LGN_OK", "LGN_ERR_INVALID_ARG", "LGN_ERR_UNSUPPORTED", "LGN_ERR_HIP"][s])
+    assert lgn.lgn_status_string(99) == "unknown lgn_status"
+    assert re.fullmatch(r"\d+\.\d+\.\d+", lgn.lgn_version())
+
+
+def test_workspace_bytes():
+    assert lgn.lgn_twopass_workspace_bytes(32768, 4096) == 32768 * 4096 * 4
+    assert lgn.lgn_twopass_workspace_bytes(0, 16) == 0
+    assert lgn.lgn_twopass_workspace_bytes(-1, 16) == 0
+
+
+def test_fused_supported():
+    F32, BF16 = lgn.DTYPE_F32, lgn.DTYPE_BF16
+    assert lgn.lgn_fused_supported(F32, 32768, 1024, 4096, 64)
+    assert lgn.lgn_fused_supported(BF16, 32768, 1024, 4096, 64)
+    assert lgn.lgn_fused_supported(F32, 16384, 2048, 8192, 8)
+    assert lgn.lgn_fused_supported(F32, 64, 32, 128, 8)
+    for cg in (8, 16, 32, 64, 128, 256, 512, 1024):
+        assert lgn.lgn_fused_supported(F32, 5, 8, 4 * cg, 4)
+    assert not lgn.lgn_fused_supported(F32, 64, 32, 96, 8)       # 12 channels per group
+    assert not lgn.lgn_fused_supported(F32, 64, 32, 2048, 1)     # 2048 per group
+    assert not lgn.lgn_fused_supported(BF16, 64, 12, 128, 8)     # K % 8 != 0 for bf16
+    assert lgn.lgn_fused_supported(F32, 64, 12, 128, 8)          # K % 4 == 0 is fine for fp32
+    assert not lgn.lgn_fused_supported(F32, 64, 32, 128, 3)      # N % G != 0
+    assert not lgn.lgn_fused_supported(2, 64, 32, 128, 8)        # unknown dtype
+
+
+def _call(fn, **kw):
+    a = dict(x=A, W=A, b_lin=A, b_add=A, gamma=A, beta=A, out=A, **GOOD)
+    a.update(kw)
+    args = [a["x"], a["W"], a["b_lin"], a["b_add"], a["gamma"], a["beta"], a["M"], a["K"], a["N"],
+            a["G"], a["eps"], a["out"]]
+    if "twopass" in fn.__name__:
+        args += [a.get("ws", A), a.get("ws_bytes", 1 << 40)]
+    return fn(*args, stream=0)
+
+
+FNS = [lgn.lgn_forward_f32, lgn.lgn_forward_bf16, lgn.lgn_forward_twopass_f32,
+       lgn.lgn_forward_twopass_bf16]
+INVALID = [
+    dict(M=-1), dict(K=-1), dict(N=0), dict(G=0), dict(G=-2), dict(N=128, G=3),
+    dict(eps=0.0), dict(eps=-1e-5), dict(eps=math.nan), dict(eps=math.inf),
+    dict(b_lin=None), dict(b_add=None), dict(gamma=None), dict(beta=None), dict(out=None),
+    dict(x=None), dict(W=None),
+]
+UNSUPPORTED = [dict(K=6), dict(N=126, G=2), dict(x=A + 4), dict(W=A + 8), dict(out=A + 4),
+               dict(gamma=A + 2)]
+
+
+@pytest.mark.parametrize("fn", FNS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("bad", INVALID, ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_invalid_arguments(fn, bad):
+    assert _call(fn, **bad) == lgn.LGN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", FNS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("bad", UNSUPPORTED, ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_unsupported_shapes(fn, bad):
+    assert _call(fn, **bad) == lgn.LGN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", [lgn.lgn_forward_f32, lgn.lgn_forward_bf16], ids=lambda f: f.__name__)
+def test_fused_rejects_uncovered_group_width(fn):
+    assert _call(fn, N=96, G=8) == lgn.LGN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", [lgn.lgn_forward_twopass_f32, lgn.lgn_forward_twopass_bf16],
+                         ids=lambda f: f.__name__)
+def test_twopass_workspace_checks(fn):
+    need = lgn.lgn_twopass_workspace_bytes(GOOD["M"], GOOD["N"])
+    assert _call(fn, ws=None) == lgn.LGN_ERR_INVALID_ARG
+    assert _call(fn, ws_bytes=need - 1) == lgn.LGN_ERR_INVALID_ARG
+    assert _call(fn, ws=A + 4, ws_bytes=need) == lgn.LGN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", FNS, ids=lambda f: f.__name__)
+def test_empty_batch_is_a_no_op(fn):
+    # M == 0 returns before any HIP call, with null data pointers
+    assert _call(fn, M=0, x=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK
+
+
+def test_binding_rejects_non_contiguous_tensor():
+    import torch
+    t = torch.zeros(8, 8).t()
+    with pytest.raises(ValueError):
+        lgn._ptr(t, "f32")
+    with pytest.raises(ValueError):
+        lgn._ptr(torch.zeros(4, dtype=torch.float64), "f32")

@@ -1,0 +1,214 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (max abs error over every compared element): 2e-4 for fp32
+inputs, 3e-2 for bf16 inputs (the oracle then runs on the same bf16 values,
+widened exactly).  Small shapes are compared element by element in full; the
+full-size workloads are compared on sampled rows (each output row depends only
+on its own input row) plus properties checked on every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gemm_activation_groupnorm_amd import lgn
+from gemm_activation_groupnorm_amd.inputs import WORKLOADS, sample_rows, workload_inputs
+from gpu_helpers import TOL, case, log, max_err, oracle_rows, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ["fused", "twopass"]
+
+
+def _check(M, K, N, G, dtype, variant, seed, eps=1e-5, x_scale=1.0):
+    log("case M=%d K=%d N=%d G=%d dtype=%s variant=%s seed=%d" % (M, K, N, G, dtype, variant, seed))
+    inp = case(M, K, N, G, seed, dtype, x_scale)
+    dev = to_device(inp, dtype)
+    y = run(dev, M, K, N, G, eps, dtype, variant)
+    torch.cuda.synchronize()
+    err = max_err(y.cpu().numpy(), oracle_rows(inp, G, eps))
+    log("  max abs err %.3e" % err)
+    assert err <= TOL[dtype], "max abs err %.3e > %.1e" % (err, TOL[dtype])
+    return err
+
+
+# ---- the two small workloads, in full, both variants, both input types ----
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("wi", [0, 1])
+def test_small_workloads_full(wi, dtype, variant):
+    w = WORKLOADS[wi]
+    _check(w.M, w.K, w.N, w.G, dtype, variant, w.seed, w.eps)
+
+
+# ---- every group width the fused kernel covers, ragged M/N/K tiles ----
+
+SHAPES = [
+    # M,   K,   N,    G     (channels per group)
+    (77, 64, 128, 16),      # 8
+    (200, 96, 256, 16),     # 16
+    (130, 40, 256, 8),      # 32, K not a multiple of the stage
+    (129, 72, 192, 3),      # 64, last channel tile half empty
+    (1, 64, 256, 4),        # 64, a single row
+    (96, 136, 384, 3),      # 128
+    (150, 64, 1280, 5),     # 256, 5 tiles
+    (70, 48, 1536, 3),      # 512
+    (65, 32, 3072, 3),      # 1024, 3 tiles, ragged M
+    (33, 8, 128, 8),        # tiny K (one chunk)
+    (40, 0, 128, 8),        # K = 0: the linear layer is its bias
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "M%d_K%d_N%d_G%d" % s)
+def test_shapes(shape, dtype, variant):
+    M, K, N, G = shape
+    _check(M, K, N, G, dtype, variant, seed=100 + M + K + N + G)
+
+
+# ---- group widths only the two-pass path covers ----
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(50, 32, 96, 8), (37, 16, 12, 4), (20, 24, 8, 4),
+                                   (9, 32, 2048, 1), (12, 40, 1200, 10)],
+                         ids=lambda s: "M%d_K%d_N%d_G%d" % s)
+def test_twopass_other_group_widths(shape, dtype):
+    M, K, N, G = shape
+    assert not lgn.lgn_fused_supported(0 if dtype == "f32" else 1, M, K, N, G)
+    _check(M, K, N, G, dtype, "twopass", seed=7 + N)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_one_channel_per_group_gives_beta(variant):
+    M, K, N = 10, 32, 64
+    inp = case(M, K, N, N, 3)
+    dev = to_device(inp, "f32")
+    if variant == "fused":
+        assert lgn.lgn_forward_f32(dev["x"], dev["W"], dev["b_lin"], dev["b_add"], dev["gamma"],
+                                   dev["beta"], M, K, N, N, 1e-5,
+                                   torch.empty(M, N, device="cuda")) == lgn.LGN_ERR_UNSUPPORTED
+        return
+    y = run(dev, M, K, N, N, 1e-5, "f32", "twopass").cpu().numpy()
+    assert np.array_equal(y, np.broadcast_to(inp["beta"], (M, N)))
+
+
+# ---- the full-size workloads: sampled rows + properties of every row ----
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("wi", [2, 3, 4])
+def test_full_size_workloads_sampled(wi, variant):
+    w = WORKLOADS[wi]
+    log("workload %s variant=%s" % (w.name, variant))
+    inp = workload_inputs(w)
+    dev = to_device(inp, w.dtype)
+    y = run(dev, w.M, w.K, w.N, w.G, w.eps, w.dtype, variant)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.M, 48, seed=w.seed)
+    err = max_err(y[torch.from_numpy(rows).cuda()].cpu().numpy(),
+                  oracle_rows(inp, w.G, w.eps, rows))
+    log("  sampled-row max abs err %.3e" % err)
+    assert err <= TOL[w.dtype]
+    # every row: finite, and undoing the affine gives per-group mean 0 and
+    # variance v/(v+eps) <= 1 (close to 1 here since v >> eps)
+    assert bool(torch.isfinite(y).all())
+    gamma, beta = dev["gamma"], dev["beta"]
+    C = w.N // w.G
+    for r0 in range(0, w.M, 4096):
+        n = ((y[r0:r0 + 4096] - beta) / gamma).double().view(-1, w.G, C)
+        mu = n.mean(dim=2)
+        var = n.var(dim=2, unbiased=False)
+        assert float(mu.abs().max()) < 2e-3
+        assert float(var.max()) < 1.0 + 2e-3 and float(var.min()) > 0.99
+
+
+# ---- determinism, row independence, in place, streams, bounds ----
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bitwise_deterministic_and_row_split(variant):
+    w = WORKLOADS[1]
+    inp = workload_inputs(w)
+    dev = to_device(inp, "f32")
+    y1 = run(dev, w.M, w.K, w.N, w.G, w.eps, "f32", variant)
+    y2 = run(dev, w.M, w.K, w.N, w.G, w.eps, "f32", variant)
+    h = w.M // 2 + 3
+    top = dict(dev, x=dev["x"][:h].contiguous())
+    bot = dict(dev, x=dev["x"][h:].contiguous())
+    ya = run(top, h, w.K, w.N, w.G, w.eps, "f32", variant)
+    yb = run(bot, w.M - h, w.K, w.N, w.G, w.eps, "f32", variant)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2), "run-to-run difference"
+    assert torch.equal(torch.cat([ya, yb]), y1), "row split changes results"
+
+
+def test_twopass_in_place_matches_separate_workspace():
+    w = WORKLOADS[1]
+    inp = workload_inputs(w)
+    dev = to_device(inp, "f32")
+    y_sep = run(dev, w.M, w.K, w.N, w.G, w.eps, "f32", "twopass")
+    out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    y_in = run(dev, w.M, w.K, w.N, w.G, w.eps, "f32", "twopass", out=out, ws=out)
+    torch.cuda.synchronize()
+    assert torch.equal(y_sep, y_in)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_zero_weight_rows_identical(variant):
+    M, K, N, G = 100, 64, 256, 4
+    inp = case(M, K, N, G, 21)
+    inp["W"][:] = 0.0
+    inp["b_lin"][:] = 0.0
+    dev = to_device(inp, "f32")
+    y = run(dev, M, K, N, G, 1e-5, "f32", variant).cpu().numpy()
+    assert np.all(y == y[:1]), "with W = 0 every row must be identical"
+    assert max_err(y[:1], oracle_rows(inp, G, 1e-5, np.array([0]))) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_group_shift_invariance(variant):
+    M, K, N, G = 64, 64, 512, 8
+    inp = case(M, K, N, G, 22)
+    dev = to_device(inp, "f32")
+    y0 = run(dev, M, K, N, G, 1e-5, "f32", variant)
+    shift = torch.repeat_interleave(torch.linspace(-2, 2, G), N // G).cuda()
+    y1 = run(dict(dev, b_add=(dev["b_add"] + shift).contiguous()), M, K, N, G, 1e-5, "f32",
+             variant)
+    torch.cuda.synchronize()
+    assert float((y0 - y1).abs().max()) <= 1e-4
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_no_writes_outside_output(variant):
+    M, K, N, G = 131, 64, 192, 3
+    inp = case(M, K, N, G, 23)
+    dev = to_device(inp, "f32")
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
+    out_ptr = buf.data_ptr() + pad * 4
+    args = (dev["x"], dev["W"], dev["b_lin"], dev["b_add"], dev["gamma"], dev["beta"],
+            M, K, N, G, 1e-5, out_ptr)
+    if variant == "fused":
+        lgn.check(lgn.lgn_forward_f32(*args))
+    else:
+        lgn.check(lgn.lgn_forward_twopass_f32(*args, out_ptr, M * N * 4))
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == 12345.0).all()) and bool((buf[pad + M * N:] == 12345.0).all())
+    y = buf[pad:pad + M * N].view(M, N).cpu().numpy()
+    assert max_err(y, oracle_rows(inp, G, 1e-5)) <= TOL["f32"]
+
+
+def test_side_stream_and_empty_batch():
+    w = WORKLOADS[0]
+    inp = workload_inputs(w)
+    dev = to_device(inp, "f32")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        lgn.check(lgn.lgn_forward_f32(dev["x"], dev["W"], dev["b_lin"], dev["b_add"],
+                                      dev["gamma"], dev["beta"], w.M, w.K, w.N, w.G, w.eps, out,
+                                      stream=s))
+    s.synchronize()
+    assert max_err(out.cpu().numpy(), oracle_rows(inp, w.G, w.eps)) <= TOL["f32"]
+    assert lgn.lgn_forward_f32(None, dev["W"], dev["b_lin"], dev["b_add"], dev["gamma"],
+                               dev["beta"], 0, w.K, w.N, w.G, w.eps, None) == lgn.LGN_OK
