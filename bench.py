@@ -172,6 +172,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (bf16, wide group, two-pass)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the forward, run 5 plain device copies of MIB MiB (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -183,6 +186,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "copies": 5}), flush=True)
+        return
     from gemm_activation_groupnorm_amd import build as hip_build
     if not os.path.exists(hip_build.LIB):
         hip_build.build()
