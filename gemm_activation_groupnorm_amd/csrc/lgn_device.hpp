@@ -44,10 +44,13 @@ template <> struct dt_traits<bf16_t> {
 // ---------------------------------------------------------------- tiles ----
 // BS samples x BC channels per workgroup; WAVES_S x WAVES_C waves; each wave
 // owns WS x WC = (32*TS) x (32*TC) of the tile.  ROWB bytes of K per LDS row.
-template <class DT, int BS_, int BC_, int WAVES_S_, int WAVES_C_, int ROWB_>
+// OCC = waves per SIMD the kernel must fit (register budget 512/OCC per
+// lane, accumulators included).
+template <class DT, int BS_, int BC_, int WAVES_S_, int WAVES_C_, int ROWB_, int OCC_ = 1>
 struct TileCfg {
     static constexpr int BS = BS_, BC = BC_, WAVES_S = WAVES_S_, WAVES_C = WAVES_C_;
     static constexpr int ROWB = ROWB_;
+    static constexpr int OCC = OCC_;
     static constexpr int NT = 64 * WAVES_S * WAVES_C;
     static constexpr int WS = BS / WAVES_S, WC = BC / WAVES_C;
     static constexpr int TS = WS / 32, TC = WC / 32;
@@ -100,8 +103,8 @@ template <> struct Mfma<bf16_t> {
 };
 
 // ----------------------------------------------------------- GEMM core ----
-// Accumulates acc[ts][tc] (32 samples x 32 channels each) for the workgroup
-// tile at (m0, n0) over the whole K range.  Global -> register prefetch of the
+// Adds to acc[ts][tc] (32 samples x 32 channels each; the caller sets the
+// initial value) the products of the workgroup tile at (m0, n0) over K.  Global -> register prefetch of the
 // next stage overlaps the MFMAs of the current one; two LDS stages, one
 // barrier per stage.  Rows past M or N and K past the end load as zeros.
 template <class DT, class Cfg>
@@ -177,12 +180,6 @@ struct GemmCore {
                                                int M, int N, int K, int m0, int n0,
                                                unsigned char *smem, int tid, int wc0, int ws0,
                                                int lr, int h, f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
-#pragma unroll
-        for (int ts = 0; ts < Cfg::TS; ++ts)
-#pragma unroll
-            for (int tc = 0; tc < Cfg::TC; ++tc)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[ts][tc][r] = 0.0f;
 
         const int KT = (K + Cfg::BK - 1) / Cfg::BK;
         if (KT == 0) return;
@@ -200,6 +197,149 @@ struct GemmCore {
             __syncthreads();
         }
     }
+};
+
+// --------------------------------------------- GEMM core, LDS DMA ring ----
+// Same contract as GemmCore, for K a multiple of the stage depth BK.
+// Operands go global -> LDS directly (global_load_lds_dwordx4: each lane's
+// 16 bytes land at the wave-uniform LDS base + 16 * lane), so no registers
+// hold staged data and STAGES-1 stages are in flight while one is consumed.
+// The swizzle is applied on the global side: the lane that fills physical
+// chunk p of LDS row r fetches logical chunk p ^ f(r).  Rows past M or N are
+// clamped to the last row (their results are never stored).
+//
+// Synchronisation per stage kt (one barrier):
+//   s_waitcnt vmcnt(<loads issued after stage kt>)  -- my part of stage kt landed
+//   s_barrier                                       -- everyone's part landed, and
+//                                                      everyone finished stage kt-1
+//   issue stage kt+STAGES-1 into the ring slot of stage kt-1
+//   ds_read + MFMA on stage kt
+// Every wave's LDS reads of a stage complete before its next barrier (the
+// MFMAs that consume them wait on lgkmcnt), so a slot is refilled only after
+// all waves are done with it.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    compiler_fence();
+}
+
+__device__ __forceinline__ void block_barrier() {
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
+template <class DT, class Cfg, int STAGES>
+struct GemmCoreDMA {
+    typedef typename dt_traits<DT>::storage T;
+    static constexpr int NW = Cfg::NT / 64;
+    static constexpr int NB = Cfg::STAGE_BYTES / 1024;   // 1 KiB blocks per stage
+    static constexpr int BPW = (NB + NW - 1) / NW;       // blocks per wave per stage
+    static constexpr int ROWS_PER_BLOCK = 1024 / Cfg::ROWB;
+    static_assert(Cfg::STAGE_BYTES % 1024 == 0, "whole 1 KiB blocks per stage");
+    static_assert((Cfg::BC * Cfg::ROWB) % 1024 == 0, "W and x rows never share a block");
+    static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+    static_assert((STAGES - 2) * BPW < 64, "vmcnt range");
+    static constexpr int SMEM_BYTES = STAGES * Cfg::STAGE_BYTES;
+
+    // Block j of a wave.  When the blocks do not divide evenly, the spare
+    // loads of the last waves repeat block NB-1: the same bytes to the same
+    // LDS location, so every wave issues exactly BPW loads per stage and the
+    // vmcnt arithmetic is the same for all waves.
+    static __device__ __forceinline__ int block_of(int wave, int j) {
+        const int b = wave * BPW + j;
+        return b < NB ? b : NB - 1;
+    }
+
+    // Per-lane source pointer (k = 0) of each block this wave fills.
+    static __device__ __forceinline__ void setup(const T *__restrict__ x, const T *__restrict__ W,
+                                                 int M, int N, int K, int m0, int n0, int wave,
+                                                 int lane, const unsigned char *(&src)[BPW]) {
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            const int b = block_of(wave, j);
+            const int o = b * 1024 + 16 * lane;
+            const int r = o / Cfg::ROWB;
+            const int p = (o % Cfg::ROWB) / 16;
+            const int c = swz<Cfg>(r, p);   // XOR swizzle is its own inverse
+            const T *row;
+            if (b * ROWS_PER_BLOCK < Cfg::BC) {
+                int n = n0 + r;
+                n = n < N ? n : N - 1;
+                row = W + (size_t)n * (size_t)K;
+            } else {
+                int m = m0 + (r - Cfg::BC);
+                m = m < M ? m : M - 1;
+                row = x + (size_t)m * (size_t)K;
+            }
+            src[j] = reinterpret_cast<const unsigned char *>(row + c * Cfg::EPC);
+        }
+    }
+
+    static __device__ __forceinline__ void issue(unsigned char *smem, int slot, int wave, int kt,
+                                                 const unsigned char *const (&src)[BPW]) {
+        const size_t koff = (size_t)kt * (Cfg::BK * Cfg::EB);
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            unsigned char *dst = smem + slot * Cfg::STAGE_BYTES + block_of(wave, j) * 1024;
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(src[j] + koff), (lds_void_t *)dst, 16,
+                                             0, 0);
+        }
+    }
+
+    // Wait until at most `after` stages (issued after the one needed) are in flight.
+    static __device__ __forceinline__ void wait_stage(int after) {
+        if constexpr (STAGES >= 4) {
+            if (after >= 2) { wait_vmcnt<2 * BPW>(); return; }
+        }
+        if constexpr (STAGES >= 3) {
+            if (after >= 1) { wait_vmcnt<BPW>(); return; }
+        }
+        wait_vmcnt<0>();
+    }
+
+    static __device__ __forceinline__ void run(const T *__restrict__ x, const T *__restrict__ W,
+                                               int M, int N, int K, int m0, int n0,
+                                               unsigned char *smem, int tid, int wc0, int ws0,
+                                               int lr, int h, f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+        const int KT = K / Cfg::BK;
+        if (KT == 0) return;
+        const int wave = tid >> 6, lane = tid & 63;
+        const unsigned char *src[BPW];
+        setup(x, W, M, N, K, m0, n0, wave, lane, src);
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < KT) issue(smem, s, wave, s, src);
+        for (int kt = 0; kt < KT; ++kt) {
+            const int last_issued = kt + STAGES - 2 < KT - 1 ? kt + STAGES - 2 : KT - 1;
+            wait_stage(last_issued - kt);
+            block_barrier();
+            if (kt + STAGES - 1 < KT) issue(smem, (kt + STAGES - 1) % STAGES, wave, kt + STAGES - 1, src);
+            GemmCore<DT, Cfg>::compute_stage(smem + (kt % STAGES) * Cfg::STAGE_BYTES, wc0, ws0, lr,
+                                             h, acc);
+        }
+    }
+};
+
+// Core selector: RING == 0 is the register-staged GemmCore (two LDS stages,
+// any K); RING >= 2 is the LDS DMA ring of that depth (K % BK == 0).
+template <class DT, class Cfg, int RING>
+struct CoreSel {
+    typedef GemmCoreDMA<DT, Cfg, RING> type;
+    static constexpr int SMEM = RING * Cfg::STAGE_BYTES;
+};
+template <class DT, class Cfg>
+struct CoreSel<DT, Cfg, 0> {
+    typedef GemmCore<DT, Cfg> type;
+    static constexpr int SMEM = 2 * Cfg::STAGE_BYTES;
 };
 
 // ------------------------------------------------------ tile schedule ----

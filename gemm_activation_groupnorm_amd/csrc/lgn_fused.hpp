@@ -21,10 +21,37 @@
 
 namespace lgn {
 
+// Per-channel vectors of the tile, staged once into LDS: [4][BC] floats
+// (b_lin, b_add, gamma, beta); channels past N read as 0.
+template <int BC>
+struct TileParams {
+    static constexpr int BYTES = 4 * BC * 4;
+    static __device__ __forceinline__ void stage(float *lds, const float *__restrict__ b_lin,
+                                                 const float *__restrict__ b_add,
+                                                 const float *__restrict__ gamma,
+                                                 const float *__restrict__ beta, int n0, int N,
+                                                 int tid, int nt) {
+        for (int i = tid; i < BC; i += nt) {
+            const int n = n0 + i;
+            const bool ok = n < N;
+            lds[i] = ok ? b_lin[n] : 0.f;
+            lds[BC + i] = ok ? b_add[n] : 0.f;
+            lds[2 * BC + i] = ok ? gamma[n] : 0.f;
+            lds[3 * BC + i] = ok ? beta[n] : 0.f;
+        }
+    }
+    // 4 consecutive channels starting at tile channel c (c % 4 == 0) of vector v.
+    static __device__ __forceinline__ f32x4 get(const float *lds, int v, int c) {
+        return *reinterpret_cast<const f32x4 *>(lds + v * BC + c);
+    }
+};
+
 // CG = channels per group (power of two, 8 .. 1024).  The tile's channel
 // span BC is a multiple of CG, so every group lies inside one workgroup.
-template <class DT, class Cfg, int CG>
-__global__ __launch_bounds__(Cfg::NT) void lgn_fused_kernel(
+// RING selects the GEMM core (0: register-staged, any K; >= 2: LDS DMA ring).
+template <class DT, class Cfg, int CG, int RING>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC)))
+void lgn_fused_kernel(
     const typename dt_traits<DT>::storage *__restrict__ x,
     const typename dt_traits<DT>::storage *__restrict__ W, const float *__restrict__ b_lin,
     const float *__restrict__ b_add, const float *__restrict__ gamma,
@@ -41,7 +68,10 @@ __global__ __launch_bounds__(Cfg::NT) void lgn_fused_kernel(
     static_assert(WPG == 1 || NSEG == 1, "a cross-wave group fills the wave's channel span");
     static_assert(WPG <= Cfg::WAVES_C, "group wider than the tile");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * Cfg::STAGE_BYTES];
+    typedef CoreSel<DT, Cfg, RING> Sel;
+    typedef TileParams<Cfg::BC> Par;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Sel::SMEM + Par::BYTES];
+    float *par = reinterpret_cast<float *>(smem + Sel::SMEM);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -58,69 +88,110 @@ __global__ __launch_bounds__(Cfg::NT) void lgn_fused_kernel(
     const int m0 = tm * Cfg::BS;
     const int n0 = tn * Cfg::BC;
 
-    f32x16 acc[TS][TC];
-    GemmCore<DT, Cfg>::run(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
+    Par::stage(par, b_lin, b_add, gamma, beta, n0, N, tid, Cfg::NT);
+    __syncthreads();
 
-    // ---- bias, Swish, bias (in registers) ----
+    // Accumulators start at the linear bias of their channel.
+    f32x16 acc[TS][TC];
 #pragma unroll
-    for (int tc = 0; tc < TC; ++tc) {
+    for (int tc = 0; tc < TC; ++tc)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int c = n0 + wc0 + 32 * tc + 8 * q + 4 * h;
-            float bl[4] = {0.f, 0.f, 0.f, 0.f}, ba[4] = {0.f, 0.f, 0.f, 0.f};
-            if (c < N) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bl[j] = b_lin[c + j];
-                    ba[j] = b_add[c + j];
-                }
-            }
+            const f32x4 bl = Par::get(par, 0, wc0 + 32 * tc + 8 * q + 4 * h);
 #pragma unroll
             for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
+                for (int j = 0; j < 4; ++j) acc[ts][tc][4 * q + j] = bl[j];
+        }
+    Sel::type::run(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
+
+    // ---- Swish, then the external bias (in registers) ----
+    auto activate = [&](int ts) {
+#pragma unroll
+        for (int tc = 0; tc < TC; ++tc)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 ba = Par::get(par, 1, wc0 + 32 * tc + 8 * q + 4 * h);
+#pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[ts][tc][4 * q + j] = swish(acc[ts][tc][4 * q + j] + bl[j]) + ba[j];
-        }
-    }
-
-    // ---- per-lane local statistics and the lane-half merge ----
-    float mean[TS][NSEG], m2[TS][NSEG];
-#pragma unroll
-    for (int ts = 0; ts < TS; ++ts) {
-#pragma unroll
-        for (int s = 0; s < NSEG; ++s) {
-            float sum = 0.f;
-#pragma unroll
-            for (int f = s * NLOC; f < (s + 1) * NLOC; ++f) sum += acc[ts][f / 16][f % 16];
-            const float mu = sum * (1.0f / NLOC);
-            float q2 = 0.f;
-#pragma unroll
-            for (int f = s * NLOC; f < (s + 1) * NLOC; ++f) {
-                const float d = acc[ts][f / 16][f % 16] - mu;
-                q2 += d * d;
+                    acc[ts][tc][4 * q + j] = swish(acc[ts][tc][4 * q + j]) + ba[j];
             }
-            mean[ts][s] = mu;
-            m2[ts][s] = q2;
-            merge_halves(mean[ts][s], m2[ts][s], (float)NLOC);
+    };
+    // ---- per-lane local statistics of segment s, merged with lane^32 ----
+    auto local_stats = [&](int ts, int s, float &mean, float &m2) {
+        float sum = 0.f;
+#pragma unroll
+        for (int f = s * NLOC; f < (s + 1) * NLOC; ++f) sum += acc[ts][f / 16][f % 16];
+        const float mu = sum * (1.0f / NLOC);
+        float q2 = 0.f;
+#pragma unroll
+        for (int f = s * NLOC; f < (s + 1) * NLOC; ++f) {
+            const float d = acc[ts][f / 16][f % 16] - mu;
+            q2 += d * d;
         }
-    }
+        mean = mu;
+        m2 = q2;
+        merge_halves(mean, m2, (float)NLOC);
+    };
+    // ---- normalise, affine, one 16-byte store per 4 channels ----
+    //   y = (u - mean) * rstd * gamma + beta = fma(fma(u, rstd, -mean*rstd), gamma, beta)
+    auto finish = [&](int ts, const float *rstd, const float *nmr) {
+        const int m = m0 + ws0 + 32 * ts + lr;
+#pragma unroll
+        for (int tc = 0; tc < TC; ++tc)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ct = wc0 + 32 * tc + 8 * q + 4 * h;
+                const int s = (tc * 16 + 4 * q) / NLOC;
+                const f32x4 g = Par::get(par, 2, ct);
+                const f32x4 bt = Par::get(par, 3, ct);
+                f32x4 y;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    y[j] = __builtin_fmaf(__builtin_fmaf(acc[ts][tc][4 * q + j], rstd[s], nmr[s]),
+                                          g[j], bt[j]);
+                if (m < M && n0 + ct < N)
+                    *reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + n0 + ct) = y;
+            }
+    };
 
-    // ---- groups wider than a wave: merge the waves' partials through LDS ----
-    if constexpr (WPG > 1) {
-        static_assert(Cfg::WAVES_C * Cfg::BS * 8 <= 2 * Cfg::STAGE_BYTES, "partials fit in LDS");
+    if constexpr (WPG == 1) {
+        // every group inside this wave: one sample tile at a time
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts) {
+            activate(ts);
+            float rstd[NSEG], nmr[NSEG];
+#pragma unroll
+            for (int s = 0; s < NSEG; ++s) {
+                float mean, m2;
+                local_stats(ts, s, mean, m2);
+                rstd[s] = __builtin_amdgcn_rsqf(m2 * (1.0f / CG) + eps);
+                nmr[s] = -mean * rstd[s];
+            }
+            finish(ts, rstd, nmr);
+        }
+    } else {
+        // groups span WPG waves: merge the waves' partials through LDS
+        static_assert(Cfg::WAVES_C * Cfg::BS * 8 <= Sel::SMEM, "partials fit in LDS");
+        float mean[TS], m2[TS];
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts) {
+            activate(ts);
+            local_stats(ts, 0, mean[ts], m2[ts]);
+        }
         float2 *part = reinterpret_cast<float2 *>(smem);   // [WAVES_C][BS]
         __syncthreads();   // the main loop's last LDS reads are done
         if (h == 0) {
 #pragma unroll
             for (int ts = 0; ts < TS; ++ts)
-                part[wcI * Cfg::BS + ws0 + 32 * ts + lr] = make_float2(mean[ts][0], m2[ts][0]);
+                part[wcI * Cfg::BS + ws0 + 32 * ts + lr] = make_float2(mean[ts], m2[ts]);
         }
         __syncthreads();
         const int first = (wcI / WPG) * WPG;
 #pragma unroll
         for (int ts = 0; ts < TS; ++ts) {
             const int srow = ws0 + 32 * ts + lr;
-            float2 p = part[first * Cfg::BS + srow];
+            const float2 p = part[first * Cfg::BS + srow];
             float mu = p.x, q2 = p.y;
 #pragma unroll
             for (int j = 1; j < WPG; ++j) {
@@ -130,42 +201,10 @@ __global__ __launch_bounds__(Cfg::NT) void lgn_fused_kernel(
                 mu = mu + d * (1.0f / (float)(j + 1));
                 q2 = q2 + o.y + d * d * ((float)Cfg::WC * (float)j / (float)(j + 1));
             }
-            mean[ts][0] = mu;
-            m2[ts][0] = q2;
-        }
-    }
-
-    // ---- normalise, affine, one 16-byte store per 4 channels ----
-    float rstd[TS][NSEG];
-#pragma unroll
-    for (int ts = 0; ts < TS; ++ts)
-#pragma unroll
-        for (int s = 0; s < NSEG; ++s)
-            rstd[ts][s] = __builtin_amdgcn_rsqf(m2[ts][s] * (1.0f / CG) + eps);
-
-#pragma unroll
-    for (int tc = 0; tc < TC; ++tc) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = n0 + wc0 + 32 * tc + 8 * q + 4 * h;
-            if (c >= N) continue;
-            float g[4], bt[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                g[j] = gamma[c + j];
-                bt[j] = beta[c + j];
-            }
-#pragma unroll
-            for (int ts = 0; ts < TS; ++ts) {
-                const int m = m0 + ws0 + 32 * ts + lr;
-                if (m >= M) continue;
-                const int s = (tc * 16 + 4 * q) / NLOC;
-                f32x4 y;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    y[j] = (acc[ts][tc][4 * q + j] - mean[ts][s]) * rstd[ts][s] * g[j] + bt[j];
-                *reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + c) = y;
-            }
+            float rstd[1], nmr[1];
+            rstd[0] = __builtin_amdgcn_rsqf(q2 * (1.0f / CG) + eps);
+            nmr[0] = -mu * rstd[0];
+            finish(ts, rstd, nmr);
         }
     }
 }

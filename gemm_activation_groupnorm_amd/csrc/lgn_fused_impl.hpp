@@ -14,7 +14,7 @@ namespace lgn {
 //   CG == 256 : 128 x 256, 2 x 2 waves of 64 x 128       (2 waves per group)
 //   CG == 512 :  64 x 512, 1 x 4 waves of 64 x 128       (4 waves per group)
 //   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128      (8 waves per group)
-template <class DT, class Cfg, int CG>
+template <class DT, class Cfg, int CG, int RING>
 hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
                             const typename dt_traits<DT>::storage *W, const float *b_lin,
                             const float *b_add, const float *gamma, const float *beta, int M,
@@ -23,9 +23,23 @@ hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
     const int tiles_n = (N + Cfg::BC - 1) / Cfg::BC;
     const long long blocks = (long long)tiles_m * tiles_n;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    return launch_kernel(lgn_fused_kernel<DT, Cfg, CG>, dim3((unsigned)blocks), dim3(Cfg::NT),
-                         stream, x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, tiles_m,
-                         tiles_n);
+    return launch_kernel(lgn_fused_kernel<DT, Cfg, CG, RING>, dim3((unsigned)blocks),
+                         dim3(Cfg::NT), stream, x, W, b_lin, b_add, gamma, beta, M, K, N, eps,
+                         out, tiles_m, tiles_n);
+}
+
+// The LDS DMA ring needs K to be a multiple of its stage depth; any other K
+// takes the register-staged core (zero-filled K tail).
+template <class DT, class Fast, int RING, class Slow, int CG>
+hipError_t launch_fused_pick(const typename dt_traits<DT>::storage *x,
+                             const typename dt_traits<DT>::storage *W, const float *b_lin,
+                             const float *b_add, const float *gamma, const float *beta, int M,
+                             int K, int N, float eps, float *out, hipStream_t stream) {
+    if (K % Fast::BK == 0)
+        return launch_fused_cfg<DT, Fast, CG, RING>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps,
+                                                    out, stream);
+    return launch_fused_cfg<DT, Slow, CG, 0>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out,
+                                             stream);
 }
 
 template <class DT>
@@ -33,24 +47,35 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
                         const typename dt_traits<DT>::storage *W, const float *b_lin,
                         const float *b_add, const float *gamma, const float *beta, int M, int K,
                         int N, int G, float eps, float *out, hipStream_t stream) {
-    constexpr int RB = 128;
-    typedef TileCfg<DT, 128, 128, 2, 2, RB> C64;
-    typedef TileCfg<DT, 128, 128, 4, 1, RB> C128;
-    typedef TileCfg<DT, 128, 256, 2, 2, 64> C256;
-    typedef TileCfg<DT, 64, 512, 1, 4, 64> C512;
-    typedef TileCfg<DT, 64, 1024, 1, 8, 64> C1024;
+    // register-staged fallbacks (any K)
+    typedef TileCfg<DT, 128, 128, 2, 2, 128, 2> S64;
+    typedef TileCfg<DT, 128, 128, 4, 1, 128> S128;
+    typedef TileCfg<DT, 128, 256, 2, 2, 64> S256;
+    typedef TileCfg<DT, 64, 512, 1, 4, 64> S512;
+    typedef TileCfg<DT, 64, 1024, 1, 8, 32> S1024;
+    // LDS DMA ring tiles (K % BK == 0)
+    typedef TileCfg<DT, 256, 128, 2, 2, 64, 2> F64;
+    typedef TileCfg<DT, 256, 128, 4, 1, 64, 2> F128;
+    typedef TileCfg<DT, 128, 256, 2, 2, 64> F256;
+    typedef TileCfg<DT, 64, 512, 1, 4, 64> F512;
+    typedef TileCfg<DT, 64, 1024, 1, 8, 32> F1024;
     const int cg = N / G;
+#define LGN_CASE(C, FAST, RING, SLOW)                                                            \
+    case C:                                                                                     \
+        return launch_fused_pick<DT, FAST, RING, SLOW, C>(x, W, b_lin, b_add, gamma, beta, M, K, \
+                                                          N, eps, out, stream);
     switch (cg) {
-        case 8: return launch_fused_cfg<DT, C64, 8>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, stream);
-        case 16: return launch_fused_cfg<DT, C64, 16>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, stream);
-        case 32: return launch_fused_cfg<DT, C64, 32>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, stream);
-        case 64: return launch_fused_cfg<DT, C64, 64>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, stream);
-        case 128: return launch_fused_cfg<DT, C128, 128>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, stream);
-        case 256: return launch_fused_cfg<DT, C256, 256>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, stream);
-        case 512: return launch_fused_cfg<DT, C512, 512>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, stream);
-        case 1024: return launch_fused_cfg<DT, C1024, 1024>(x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, stream);
+        LGN_CASE(8, F64, 3, S64)
+        LGN_CASE(16, F64, 3, S64)
+        LGN_CASE(32, F64, 3, S64)
+        LGN_CASE(64, F64, 3, S64)
+        LGN_CASE(128, F128, 3, S128)
+        LGN_CASE(256, F256, 3, S256)
+        LGN_CASE(512, F512, 3, S512)
+        LGN_CASE(1024, F1024, 3, S1024)
         default: return hipErrorInvalidValue;
     }
+#undef LGN_CASE
 }
 
 }  // namespace lgn

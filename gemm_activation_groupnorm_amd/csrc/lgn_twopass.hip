@@ -5,17 +5,29 @@
 
 namespace lgn {
 
-template <class DT>
-static hipError_t launch_gemm_bias(const typename dt_traits<DT>::storage *x,
-                                   const typename dt_traits<DT>::storage *W, const float *b_lin,
-                                   int M, int K, int N, float *z, hipStream_t stream) {
-    typedef TileCfg<DT, 128, 128, 2, 2, 128> Cfg;
+template <class DT, class Cfg, int RING>
+static hipError_t launch_gemm_bias_cfg(const typename dt_traits<DT>::storage *x,
+                                       const typename dt_traits<DT>::storage *W,
+                                       const float *b_lin, int M, int K, int N, float *z,
+                                       hipStream_t stream) {
     const int tiles_m = (M + Cfg::BS - 1) / Cfg::BS;
     const int tiles_n = (N + Cfg::BC - 1) / Cfg::BC;
     const long long blocks = (long long)tiles_m * tiles_n;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    return launch_kernel(lgn_gemm_bias_kernel<DT, Cfg>, dim3((unsigned)blocks), dim3(Cfg::NT),
-                         stream, x, W, b_lin, M, K, N, z, tiles_m, tiles_n);
+    return launch_kernel(lgn_gemm_bias_kernel<DT, Cfg, RING>, dim3((unsigned)blocks),
+                         dim3(Cfg::NT), stream, x, W, b_lin, M, K, N, z, tiles_m, tiles_n);
+}
+
+// Same tiles as the fused kernel for narrow groups: the LDS DMA ring when K
+// is a multiple of its stage depth, else the register-staged core.
+template <class DT>
+static hipError_t launch_gemm_bias(const typename dt_traits<DT>::storage *x,
+                                   const typename dt_traits<DT>::storage *W, const float *b_lin,
+                                   int M, int K, int N, float *z, hipStream_t stream) {
+    typedef TileCfg<DT, 256, 128, 2, 2, 64, 2> Fast;
+    typedef TileCfg<DT, 128, 128, 2, 2, 128, 2> Slow;
+    if (K % Fast::BK == 0) return launch_gemm_bias_cfg<DT, Fast, 3>(x, W, b_lin, M, K, N, z, stream);
+    return launch_gemm_bias_cfg<DT, Slow, 0>(x, W, b_lin, M, K, N, z, stream);
 }
 
 hipError_t launch_gemm_bias_f32(const float *x, const float *W, const float *b_lin, int M,

@@ -10,12 +10,15 @@
 namespace lgn {
 
 // z[m, n] = sum_k x[m,k] W[n,k] + b_lin[n], fp32, [M, N] row-major.
-template <class DT, class Cfg>
-__global__ __launch_bounds__(Cfg::NT) void lgn_gemm_bias_kernel(
+// RING selects the GEMM core (0: register-staged, any K; >= 2: LDS DMA ring).
+template <class DT, class Cfg, int RING>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC)))
+void lgn_gemm_bias_kernel(
     const typename dt_traits<DT>::storage *__restrict__ x,
     const typename dt_traits<DT>::storage *__restrict__ W, const float *__restrict__ b_lin,
     int M, int K, int N, float *__restrict__ z, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * Cfg::STAGE_BYTES];
+    typedef CoreSel<DT, Cfg, RING> Sel;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Sel::SMEM];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -28,8 +31,21 @@ __global__ __launch_bounds__(Cfg::NT) void lgn_gemm_bias_kernel(
     const int m0 = tm * Cfg::BS;
     const int n0 = tn * Cfg::BC;
 
+    // accumulators start at the linear bias of their channel
     f32x16 acc[Cfg::TS][Cfg::TC];
-    GemmCore<DT, Cfg>::run(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
+#pragma unroll
+    for (int tc = 0; tc < Cfg::TC; ++tc)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = n0 + wc0 + 32 * tc + 8 * q + 4 * h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float bl = c < N ? b_lin[c + j] : 0.f;
+#pragma unroll
+                for (int ts = 0; ts < Cfg::TS; ++ts) acc[ts][tc][4 * q + j] = bl;
+            }
+        }
+    Sel::type::run(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
 
 #pragma unroll
     for (int tc = 0; tc < Cfg::TC; ++tc) {
@@ -37,16 +53,13 @@ __global__ __launch_bounds__(Cfg::NT) void lgn_gemm_bias_kernel(
         for (int q = 0; q < 4; ++q) {
             const int c = n0 + wc0 + 32 * tc + 8 * q + 4 * h;
             if (c >= N) continue;
-            float bl[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bl[j] = b_lin[c + j];
 #pragma unroll
             for (int ts = 0; ts < Cfg::TS; ++ts) {
                 const int m = m0 + ws0 + 32 * ts + lr;
                 if (m >= M) continue;
                 f32x4 v;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = acc[ts][tc][4 * q + j] + bl[j];
+                for (int j = 0; j < 4; ++j) v[j] = acc[ts][tc][4 * q + j];
                 *reinterpret_cast<f32x4 *>(z + (size_t)m * (size_t)N + c) = v;
             }
         }
