@@ -45,12 +45,15 @@ template <> struct dt_traits<bf16_t> {
 // BS samples x BC channels per workgroup; WAVES_S x WAVES_C waves; each wave
 // owns WS x WC = (32*TS) x (32*TC) of the tile.  ROWB bytes of K per LDS row.
 // OCC = waves per SIMD the kernel must fit (register budget 512/OCC per
-// lane, accumulators included).
-template <class DT, int BS_, int BC_, int WAVES_S_, int WAVES_C_, int ROWB_, int OCC_ = 1>
+// lane, accumulators included).  EARLY = sample tiles whose MFMAs the LDS DMA
+// core issues before the next chunk pair's LDS reads (0: reads first).
+template <class DT, int BS_, int BC_, int WAVES_S_, int WAVES_C_, int ROWB_, int OCC_ = 1,
+          int EARLY_ = 1>
 struct TileCfg {
     static constexpr int BS = BS_, BC = BC_, WAVES_S = WAVES_S_, WAVES_C = WAVES_C_;
     static constexpr int ROWB = ROWB_;
     static constexpr int OCC = OCC_;
+    static constexpr int EARLY = EARLY_;
     static constexpr int NT = 64 * WAVES_S * WAVES_C;
     static constexpr int WS = BS / WAVES_S, WC = BC / WAVES_C;
     static constexpr int TS = WS / 32, TC = WC / 32;
@@ -150,29 +153,58 @@ struct GemmCore {
         }
     }
 
-    // wc0 / ws0: first channel / sample of this wave inside the tile.
+    // Fragments of chunk pair cp: lane half h reads logical chunk 2*cp + h of
+    // its W row (a) and x row (b).  wc0 / ws0: first channel / sample of this
+    // wave inside the tile.
+    static __device__ __forceinline__ void load_frags(const unsigned char *stage, int cp, int wc0,
+                                                      int ws0, int lr, int h, u32x4 (&a)[Cfg::TC],
+                                                      u32x4 (&b)[Cfg::TS]) {
+        const int c = 2 * cp + h;
+#pragma unroll
+        for (int tc = 0; tc < Cfg::TC; ++tc) {
+            const int r = wc0 + 32 * tc + lr;
+            a[tc] = *reinterpret_cast<const u32x4 *>(stage + r * Cfg::ROWB + 16 * swz<Cfg>(r, c));
+        }
+#pragma unroll
+        for (int ts = 0; ts < Cfg::TS; ++ts) {
+            const int r = Cfg::BC + ws0 + 32 * ts + lr;
+            b[ts] = *reinterpret_cast<const u32x4 *>(stage + r * Cfg::ROWB + 16 * swz<Cfg>(r, c));
+        }
+    }
+
+    // MFMAs of sample tiles [T0, T1) against all channel tiles.
+    template <int T0 = 0, int T1 = Cfg::TS>
+    static __device__ __forceinline__ void mfma_block(const u32x4 (&a)[Cfg::TC],
+                                                      const u32x4 (&b)[Cfg::TS],
+                                                      f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+#pragma unroll
+        for (int ts = T0; ts < T1; ++ts)
+#pragma unroll
+            for (int tc = 0; tc < Cfg::TC; ++tc) Mfma<DT>::run(acc[ts][tc], a[tc], b[ts]);
+    }
+
+    // All MFMAs of one LDS stage.  Fragments are double-buffered in registers:
+    // the reads of chunk pair cp+1 are issued before the MFMAs of cp, and a
+    // scheduling barrier keeps the compiler from sinking them back next to
+    // their use, so LDS latency hides under MFMA work.
     static __device__ __forceinline__ void compute_stage(const unsigned char *stage, int wc0,
                                                          int ws0, int lr, int h,
                                                          f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+        constexpr int CP = Cfg::CPR / 2;
+        u32x4 a0[Cfg::TC], b0[Cfg::TS], a1[Cfg::TC], b1[Cfg::TS];
+        load_frags(stage, 0, wc0, ws0, lr, h, a0, b0);
 #pragma unroll
-        for (int cp = 0; cp < Cfg::CPR / 2; ++cp) {
-            const int c = 2 * cp + h;
-            u32x4 a[Cfg::TC], b[Cfg::TS];
-#pragma unroll
-            for (int tc = 0; tc < Cfg::TC; ++tc) {
-                const int r = wc0 + 32 * tc + lr;
-                a[tc] = *reinterpret_cast<const u32x4 *>(stage + r * Cfg::ROWB + 16 * swz<Cfg>(r, c));
+        for (int cp = 0; cp < CP; ++cp) {
+            if (cp % 2 == 0) {
+                if (cp + 1 < CP) load_frags(stage, cp + 1, wc0, ws0, lr, h, a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_block(a0, b0, acc);
+            } else {
+                if (cp + 1 < CP) load_frags(stage, cp + 1, wc0, ws0, lr, h, a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_block(a1, b1, acc);
             }
-#pragma unroll
-            for (int ts = 0; ts < Cfg::TS; ++ts) {
-                const int r = Cfg::BC + ws0 + 32 * ts + lr;
-                b[ts] = *reinterpret_cast<const u32x4 *>(stage + r * Cfg::ROWB + 16 * swz<Cfg>(r, c));
-            }
-#pragma unroll
-            for (int ts = 0; ts < Cfg::TS; ++ts)
-#pragma unroll
-                for (int tc = 0; tc < Cfg::TC; ++tc)
-                    Mfma<DT>::run(acc[ts][tc], a[tc], b[ts]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -239,6 +271,7 @@ __device__ __forceinline__ void block_barrier() {
 
 template <class DT, class Cfg, int STAGES>
 struct GemmCoreDMA {
+    static constexpr int EARLY = Cfg::EARLY;
     typedef typename dt_traits<DT>::storage T;
     static constexpr int NW = Cfg::NT / 64;
     static constexpr int NB = Cfg::STAGE_BYTES / 1024;   // 1 KiB blocks per stage
@@ -295,37 +328,114 @@ struct GemmCoreDMA {
         }
     }
 
-    // Wait until at most `after` stages (issued after the one needed) are in flight.
-    static __device__ __forceinline__ void wait_stage(int after) {
-        if constexpr (STAGES >= 4) {
-            if (after >= 2) { wait_vmcnt<2 * BPW>(); return; }
+    struct Frags {
+        u32x4 a[Cfg::TC];
+        u32x4 b[Cfg::TS];
+    };
+
+    // Chunk pair CPI of stage kt: `cur` holds its fragments, `nxt` receives
+    // the next ones (recursion keeps every buffer binding compile-time).
+    template <int CPI, bool HANDOVER, bool ISSUE, int AFTER>
+    static __device__ __forceinline__ void cp_step(unsigned char *smem, int kt, int KT, int wave,
+                                                   int wc0,
+                                                   int ws0, int lr, int h,
+                                                   const unsigned char *const (&src)[BPW],
+                                                   Frags &cur, Frags &nxt,
+                                                   f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+        typedef GemmCore<DT, Cfg> C;
+        constexpr int CP = Cfg::CPR / 2;
+        if constexpr (CPI + 1 < CP) {
+            // first MFMAs of this chunk pair, then the next pair's reads (their
+            // registers are free by now), then the remaining MFMAs
+            const unsigned char *stage = smem + (kt % STAGES) * Cfg::STAGE_BYTES;
+            C::template mfma_block<0, EARLY>(cur.a, cur.b, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            C::load_frags(stage, CPI + 1, wc0, ws0, lr, h, nxt.a, nxt.b);
+            __builtin_amdgcn_sched_barrier(0);
+            C::template mfma_block<EARLY, Cfg::TS>(cur.a, cur.b, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            cp_step<CPI + 1, HANDOVER, ISSUE, AFTER>(smem, kt, KT, wave, wc0, ws0, lr, h, src, nxt,
+                                                     cur, acc);
+        } else {
+            constexpr int HALF = Cfg::TS / 2 > 0 ? Cfg::TS / 2 : 1;
+            C::template mfma_block<0, HALF>(cur.a, cur.b, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (HANDOVER) {
+                compiler_fence();
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+                wait_vmcnt<AFTER * BPW>();
+                block_barrier();
+                // next stage's first reads before the DMA issue: they gate the MFMAs
+                C::load_frags(smem + ((kt + 1) % STAGES) * Cfg::STAGE_BYTES, 0, wc0, ws0, lr, h,
+                              nxt.a, nxt.b);
+                if constexpr (ISSUE)
+                    issue(smem, kt % STAGES, wave, kt + STAGES < KT ? kt + STAGES : KT - 1, src);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            C::template mfma_block<HALF, Cfg::TS>(cur.a, cur.b, acc);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (STAGES >= 3) {
-            if (after >= 1) { wait_vmcnt<BPW>(); return; }
-        }
-        wait_vmcnt<0>();
+    }
+
+    template <bool HANDOVER, bool ISSUE, int AFTER>
+    static __device__ __forceinline__ void stage_body(unsigned char *smem, int kt, int KT, int wave,
+                                                      int wc0, int ws0, int lr, int h,
+                                                      const unsigned char *const (&src)[BPW],
+                                                      Frags &fa, Frags &fb,
+                                                      f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+        cp_step<0, HANDOVER, ISSUE, AFTER>(smem, kt, KT, wave, wc0, ws0, lr, h, src, fa, fb, acc);
     }
 
     static __device__ __forceinline__ void run(const T *__restrict__ x, const T *__restrict__ W,
                                                int M, int N, int K, int m0, int n0,
                                                unsigned char *smem, int tid, int wc0, int ws0,
                                                int lr, int h, f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+        constexpr int CP = Cfg::CPR / 2;
         const int KT = K / Cfg::BK;
         if (KT == 0) return;
-        const int wave = tid >> 6, lane = tid & 63;
+        // wave index as a scalar: the DMA's LDS base (M0) is then computed on
+        // the scalar unit
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
         const unsigned char *src[BPW];
         setup(x, W, M, N, K, m0, n0, wave, lane, src);
+        // Every iteration issues exactly one stage, so the vmcnt arithmetic is
+        // the same everywhere: stage indices past the end are clamped to the
+        // last stage (L2-resident by then) and land in the slot just freed,
+        // which no later stage uses.
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < KT) issue(smem, s, wave, s, src);
-        for (int kt = 0; kt < KT; ++kt) {
-            const int last_issued = kt + STAGES - 2 < KT - 1 ? kt + STAGES - 2 : KT - 1;
-            wait_stage(last_issued - kt);
-            block_barrier();
-            if (kt + STAGES - 1 < KT) issue(smem, (kt + STAGES - 1) % STAGES, wave, kt + STAGES - 1, src);
-            GemmCore<DT, Cfg>::compute_stage(smem + (kt % STAGES) * Cfg::STAGE_BYTES, wc0, ws0, lr,
-                                             h, acc);
+        for (int s = 0; s < STAGES; ++s)
+            issue(smem, s, wave, s < KT ? s : KT - 1, src);
+        wait_vmcnt<(STAGES - 1) * BPW>();
+        block_barrier();
+        Frags fa, fb;
+        GemmCore<DT, Cfg>::load_frags(smem, 0, wc0, ws0, lr, h, fa.a, fa.b);
+        if constexpr (CP % 2 == 0) {
+            // an even number of chunk pairs leaves the next stage's first
+            // fragments back in `fa`
+            for (int kt = 0; kt + 1 < KT; ++kt)
+                stage_body<true, true, STAGES - 2>(smem, kt, KT, wave, wc0, ws0, lr, h, src, fa,
+                                                   fb, acc);
+            stage_body<false, false, 0>(smem, KT - 1, KT, wave, wc0, ws0, lr, h, src, fa, fb, acc);
+        } else {
+            // an odd number leaves them in `fb`: alternate the roles
+            int kt = 0;
+            for (; kt + 2 < KT; kt += 2) {
+                stage_body<true, true, STAGES - 2>(smem, kt, KT, wave, wc0, ws0, lr, h, src, fa,
+                                                   fb, acc);
+                stage_body<true, true, STAGES - 2>(smem, kt + 1, KT, wave, wc0, ws0, lr, h, src,
+                                                   fb, fa, acc);
+            }
+            if (KT - kt == 2) {
+                stage_body<true, true, STAGES - 2>(smem, kt, KT, wave, wc0, ws0, lr, h, src, fa,
+                                                   fb, acc);
+                stage_body<false, false, 0>(smem, kt + 1, KT, wave, wc0, ws0, lr, h, src, fb, fa,
+                                            acc);
+            } else {
+                stage_body<false, false, 0>(smem, kt, KT, wave, wc0, ws0, lr, h, src, fa, fb,
+                                            acc);
+            }
         }
+        wait_vmcnt<0>();   // no DMA may land in LDS after the main loop
     }
 };
 

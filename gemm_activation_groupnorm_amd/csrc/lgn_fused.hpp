@@ -133,30 +133,69 @@ void lgn_fused_kernel(
         m2 = q2;
         merge_halves(mean, m2, (float)NLOC);
     };
-    // ---- normalise, affine, one 16-byte store per 4 channels ----
+    // ---- normalise, affine, store ----
     //   y = (u - mean) * rstd * gamma + beta = fma(fma(u, rstd, -mean*rstd), gamma, beta)
+    // A lane holds 32-byte pieces of 32 different rows, so the wave first
+    // writes its 32 x WC block to a private LDS area (16-byte chunks XOR-
+    // swizzled by the row's low 4 bits: conflict-free both ways for rows of
+    // 64..256 channels) and reads it back row by row; each store instruction
+    // then writes WC*4 contiguous bytes per row.  When the blocks of all waves
+    // do not fit in the ring, store directly.
+    constexpr int BLK_BYTES = 32 * Cfg::WC * 4;
+    constexpr bool STAGED =
+        (Cfg::NT / 64) * BLK_BYTES <= Sel::SMEM && Cfg::WC >= 64 && Cfg::WC <= 256;
+    auto normalise = [&](int ts, int tc, int q, const float *rstd, const float *nmr) {
+        const int ct = wc0 + 32 * tc + 8 * q + 4 * h;
+        const int s = (tc * 16 + 4 * q) / NLOC;
+        const f32x4 g = Par::get(par, 2, ct);
+        const f32x4 bt = Par::get(par, 3, ct);
+        f32x4 y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            y[j] = __builtin_fmaf(__builtin_fmaf(acc[ts][tc][4 * q + j], rstd[s], nmr[s]), g[j],
+                                  bt[j]);
+        return y;
+    };
     auto finish = [&](int ts, const float *rstd, const float *nmr) {
-        const int m = m0 + ws0 + 32 * ts + lr;
+        if constexpr (STAGED) {
+            constexpr int CPRW = Cfg::WC / 4;   // 16-byte chunks per block row
+            constexpr int RPI = 64 / CPRW;      // block rows per store instruction
+            unsigned char *blk = smem + wave * BLK_BYTES;
 #pragma unroll
-        for (int tc = 0; tc < TC; ++tc)
+            for (int tc = 0; tc < TC; ++tc)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int ct = wc0 + 32 * tc + 8 * q + 4 * h;
-                const int s = (tc * 16 + 4 * q) / NLOC;
-                const f32x4 g = Par::get(par, 2, ct);
-                const f32x4 bt = Par::get(par, 3, ct);
-                f32x4 y;
+                for (int q = 0; q < 4; ++q) {
+                    const int chunk = 8 * tc + 2 * q + h;
+                    *reinterpret_cast<f32x4 *>(blk + lr * (CPRW * 16) + 16 * (chunk ^ (lr & 15))) =
+                        normalise(ts, tc, q, rstd, nmr);
+                }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    y[j] = __builtin_fmaf(__builtin_fmaf(acc[ts][tc][4 * q + j], rstd[s], nmr[s]),
-                                          g[j], bt[j]);
-                if (m < M && n0 + ct < N)
-                    *reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + n0 + ct) = y;
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int row = RPI * i + lane / CPRW;
+                const int chunk = lane % CPRW;
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(blk + row * (CPRW * 16) +
+                                                                 16 * (chunk ^ (row & 15)));
+                const int m = m0 + ws0 + 32 * ts + row;
+                const int c = n0 + wc0 + 4 * chunk;
+                if (m < M && c < N) *reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + c) = y;
             }
+        } else {
+            const int m = m0 + ws0 + 32 * ts + lr;
+#pragma unroll
+            for (int tc = 0; tc < TC; ++tc)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ct = wc0 + 32 * tc + 8 * q + 4 * h;
+                    const f32x4 y = normalise(ts, tc, q, rstd, nmr);
+                    if (m < M && n0 + ct < N)
+                        *reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + n0 + ct) = y;
+                }
+        }
     };
 
     if constexpr (WPG == 1) {
         // every group inside this wave: one sample tile at a time
+        if constexpr (STAGED) __syncthreads();   // all waves are done with the ring
 #pragma unroll
         for (int ts = 0; ts < TS; ++ts) {
             activate(ts);
@@ -188,6 +227,7 @@ void lgn_fused_kernel(
         }
         __syncthreads();
         const int first = (wcI / WPG) * WPG;
+        float rstd[TS], nmr[TS];
 #pragma unroll
         for (int ts = 0; ts < TS; ++ts) {
             const int srow = ws0 + 32 * ts + lr;
@@ -201,11 +241,12 @@ void lgn_fused_kernel(
                 mu = mu + d * (1.0f / (float)(j + 1));
                 q2 = q2 + o.y + d * d * ((float)Cfg::WC * (float)j / (float)(j + 1));
             }
-            float rstd[1], nmr[1];
-            rstd[0] = __builtin_amdgcn_rsqf(q2 * (1.0f / CG) + eps);
-            nmr[0] = -mu * rstd[0];
-            finish(ts, rstd, nmr);
+            rstd[ts] = __builtin_amdgcn_rsqf(q2 * (1.0f / CG) + eps);
+            nmr[ts] = -mu * rstd[ts];
         }
+        if constexpr (STAGED) __syncthreads();   // partials read before the block area is reused
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts) finish(ts, &rstd[ts], &nmr[ts]);
     }
 }
 

@@ -5,15 +5,18 @@
 #include "lgn_fused.hpp"
 #include "lgn_launch.hpp"
 
+#include <type_traits>
+
 namespace lgn {
 
-// Tile per channel-per-group count CG (BS samples x BC channels, waves
-// along samples x channels, LDS row bytes):
-//   CG <= 64  : 128 x 128, 2 x 2 waves of 64 x 64        (group inside a wave)
-//   CG == 128 : 128 x 128, 4 x 1 waves of 32 x 128       (group inside a wave)
-//   CG == 256 : 128 x 256, 2 x 2 waves of 64 x 128       (2 waves per group)
-//   CG == 512 :  64 x 512, 1 x 4 waves of 64 x 128       (4 waves per group)
-//   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128      (8 waves per group)
+// Tiles per channel-per-group count CG, for K a multiple of the stage depth
+// (LDS DMA ring) -- BS samples x BC channels, waves along samples x channels:
+//   CG <= 64  : 256 x 256, 2 x 4 waves of 128 x 64, ring of 4 (bf16) / 3 (fp32)
+//   CG == 128 : 256 x 128, 4 x 1 waves of 64 x 128, ring of 3
+//   CG == 256 : 128 x 256, 2 x 2 waves of 64 x 128 (2 waves per group), ring of 3
+//   CG == 512 :  64 x 512, 1 x 4 waves of 64 x 128 (4 waves per group), ring of 3
+//   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128 (8 waves per group), ring of 2
+// and register-staged tiles for any other K.
 template <class DT, class Cfg, int CG, int RING>
 hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
                             const typename dt_traits<DT>::storage *W, const float *b_lin,
@@ -54,25 +57,26 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
     typedef TileCfg<DT, 64, 512, 1, 4, 64> S512;
     typedef TileCfg<DT, 64, 1024, 1, 8, 32> S1024;
     // LDS DMA ring tiles (K % BK == 0)
-    typedef TileCfg<DT, 256, 128, 2, 2, 64, 2> F64;
+    typedef TileCfg<DT, 256, 256, 2, 4, 64, 2> F64;
+    constexpr int R64 = std::is_same<DT, bf16_t>::value ? 4 : 3;
     typedef TileCfg<DT, 256, 128, 4, 1, 64, 2> F128;
     typedef TileCfg<DT, 128, 256, 2, 2, 64> F256;
     typedef TileCfg<DT, 64, 512, 1, 4, 64> F512;
-    typedef TileCfg<DT, 64, 1024, 1, 8, 32> F1024;
+    typedef TileCfg<DT, 64, 1024, 1, 8, 64> F1024;
     const int cg = N / G;
 #define LGN_CASE(C, FAST, RING, SLOW)                                                            \
     case C:                                                                                     \
         return launch_fused_pick<DT, FAST, RING, SLOW, C>(x, W, b_lin, b_add, gamma, beta, M, K, \
                                                           N, eps, out, stream);
     switch (cg) {
-        LGN_CASE(8, F64, 3, S64)
-        LGN_CASE(16, F64, 3, S64)
-        LGN_CASE(32, F64, 3, S64)
-        LGN_CASE(64, F64, 3, S64)
+        LGN_CASE(8, F64, R64, S64)
+        LGN_CASE(16, F64, R64, S64)
+        LGN_CASE(32, F64, R64, S64)
+        LGN_CASE(64, F64, R64, S64)
         LGN_CASE(128, F128, 3, S128)
         LGN_CASE(256, F256, 3, S256)
         LGN_CASE(512, F512, 3, S512)
-        LGN_CASE(1024, F1024, 3, S1024)
+        LGN_CASE(1024, F1024, 2, S1024)
         default: return hipErrorInvalidValue;
     }
 #undef LGN_CASE

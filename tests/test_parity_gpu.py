@@ -56,6 +56,12 @@ SHAPES = [
     (65, 32, 3072, 3),      # 1024, 3 tiles, ragged M
     (33, 8, 128, 8),        # tiny K (one chunk)
     (40, 0, 128, 8),        # K = 0: the linear layer is its bias
+    # K a multiple of the DMA ring's stage depth, ragged sample/channel tiles
+    (300, 128, 320, 5),     # 64, 2 channel tiles (second 1/4 full), 2 sample tiles
+    (257, 32, 512, 8),      # 64, one bf16 stage / two fp32 stages
+    (33, 16, 256, 4),       # 64, a single fp32 stage (bf16 takes the other core)
+    (1000, 64, 768, 12),    # 64, ring shorter than its depth
+    (520, 192, 1152, 9),    # 128, ragged
 ]
 
 
