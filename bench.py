@@ -11,8 +11,8 @@ bracketed by torch.cuda.synchronize().  Prints ONE JSON line on stdout; a
 human-readable summary goes to stderr.
 
 value      : GEMM TFLOP/s of the whole timed region, 2*M*N*K*K_steps / wall time.
-roofline   : the fused kernel's own time per launch from HIP events recorded on
-             the launch stream around every timed launch, against the MI355X
+roofline   : the fused kernel's mean time per launch from one HIP event pair
+             recorded on the launch stream around the timed launches, against the MI355X
              dense MFMA peak of its input type (fp32 157.3, bf16 2500 TFLOP/s).
              traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
              counters (profiles/traffic.json), only if the kernel sources are
@@ -107,22 +107,22 @@ class Runner:
             self.launch = lambda: lgn.check(fn(*args, ws, nb, stream=s))
 
     def time(self, steps: int, warmup: int):
+        """Wall time of `steps` back-to-back launches and the mean launch
+        duration from one HIP event pair on the launch stream around them."""
         import torch
         for _ in range(warmup):
             self.launch()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        for a, b in ev:
-            a.record(self.stream)
+        start.record(self.stream)
+        for _ in range(steps):
             self.launch()
-            b.record(self.stream)
+        end.record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kms = sorted(a.elapsed_time(b) for a, b in ev)
-        return wall, kms
+        return wall, start.elapsed_time(end) / steps
 
     def check_rows(self, nrows: int = 8):
         import numpy as np
@@ -203,18 +203,16 @@ def main():
 
     w = get_workload(args.workload)
     r = Runner(w, args.variant)
-    wall, kms = r.time(args.steps, args.warmup)
+    wall, kmean = r.time(args.steps, args.warmup)
     flops = float(w.flops)
     ms_per_step = wall / args.steps * 1e3
     value = flops / (ms_per_step * 1e-3) / 1e12
-    kmean = sum(kms) / len(kms)
     achieved = flops / (kmean * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     err, nrows = r.check_rows()
-    eprint("[bench] %s/%s: %.3f ms/step, kernel mean %.3f ms (p10 %.3f, p90 %.3f) -> %.1f TFLOP/s "
-           "(%.1f%% of %.1f); sampled-row max err %.2e"
-           % (w.name, args.variant, ms_per_step, kmean, kms[len(kms) // 10],
-              kms[(len(kms) * 9) // 10], achieved, 100 * achieved / peak, peak, err))
+    eprint("[bench] %s/%s: %.3f ms/step, kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f); "
+           "sampled-row max err %.2e"
+           % (w.name, args.variant, ms_per_step, kmean, achieved, 100 * achieved / peak, peak, err))
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -257,8 +255,7 @@ def main():
                 continue
             we = get_workload(name)
             re = Runner(we, variant)
-            wl, km = re.time(20, 5)
-            km_mean = sum(km) / len(km)
+            wl, km_mean = re.time(20, 5)
             ach = we.flops / (km_mean * 1e-3) / 1e12
             e2, _ = re.check_rows(4)
             eprint("[bench] %s/%s: kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f), err %.2e"

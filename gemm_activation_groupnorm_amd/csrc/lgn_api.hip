@@ -1,7 +1,7 @@
 // lgn_api.hip -- the C ABI of liblgn.so (declared in include/lgn.h):
 // argument validation (host only, before any HIP call), the gfx950 device
 // check, and dispatch to the kernel launchers.
-#include "../../include/lgn.h"
+#include "lgn.h"
 
 #include <hip/hip_runtime.h>
 #include <math.h>

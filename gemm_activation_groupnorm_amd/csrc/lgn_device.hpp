@@ -45,14 +45,17 @@ template <> struct dt_traits<bf16_t> {
 // BS samples x BC channels per workgroup; WAVES_S x WAVES_C waves; each wave
 // owns WS x WC = (32*TS) x (32*TC) of the tile.  ROWB bytes of K per LDS row.
 // OCC = waves per SIMD the kernel must fit (register budget 512/OCC per
-// lane, accumulators included).  EARLY = sample tiles whose MFMAs the LDS DMA
-// core issues before the next chunk pair's LDS reads (0: reads first).
+// lane, accumulators included).  PIPE: the LDS DMA core reads the next
+// chunk pair's fragments under the current MFMAs (1) or reads each chunk
+// pair's fragments right before its MFMAs (0).  EARLY (PIPE only) = sample
+// tiles whose MFMAs are issued before those reads (0: reads first).
 template <class DT, int BS_, int BC_, int WAVES_S_, int WAVES_C_, int ROWB_, int OCC_ = 1,
-          int EARLY_ = 1>
+          int PIPE_ = 1, int EARLY_ = 1>
 struct TileCfg {
     static constexpr int BS = BS_, BC = BC_, WAVES_S = WAVES_S_, WAVES_C = WAVES_C_;
     static constexpr int ROWB = ROWB_;
     static constexpr int OCC = OCC_;
+    static constexpr bool PIPE = PIPE_ != 0;
     static constexpr int EARLY = EARLY_;
     static constexpr int NT = 64 * WAVES_S * WAVES_C;
     static constexpr int WS = BS / WAVES_S, WC = BC / WAVES_C;
@@ -386,6 +389,37 @@ struct GemmCoreDMA {
         cp_step<0, HANDOVER, ISSUE, AFTER>(smem, kt, KT, wave, wc0, ws0, lr, h, src, fa, fb, acc);
     }
 
+    // Simple schedule: per stage, wait for it, barrier, issue stage
+    // kt+STAGES-1 into the slot of stage kt-1, then read-and-MFMA each chunk
+    // pair.  Stage indices past the end are clamped as in run().
+    static __device__ __forceinline__ void run_simple(const T *__restrict__ x,
+                                                      const T *__restrict__ W, int M, int N, int K,
+                                                      int m0, int n0, unsigned char *smem, int tid,
+                                                      int wc0, int ws0, int lr, int h,
+                                                      f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+        typedef GemmCore<DT, Cfg> C;
+        const int KT = K / Cfg::BK;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+        const unsigned char *src[BPW];
+        setup(x, W, M, N, K, m0, n0, wave, lane, src);
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) issue(smem, s, wave, s < KT ? s : KT - 1, src);
+        for (int kt = 0; kt < KT; ++kt) {
+            wait_vmcnt<(STAGES - 2) * BPW>();
+            block_barrier();
+            const int nk = kt + STAGES - 1;
+            issue(smem, nk % STAGES, wave, nk < KT ? nk : KT - 1, src);
+            const unsigned char *stage = smem + (kt % STAGES) * Cfg::STAGE_BYTES;
+#pragma unroll
+            for (int cp = 0; cp < Cfg::CPR / 2; ++cp) {
+                u32x4 a[Cfg::TC], b[Cfg::TS];
+                C::load_frags(stage, cp, wc0, ws0, lr, h, a, b);
+                C::mfma_block(a, b, acc);
+            }
+        }
+        wait_vmcnt<0>();
+    }
+
     static __device__ __forceinline__ void run(const T *__restrict__ x, const T *__restrict__ W,
                                                int M, int N, int K, int m0, int n0,
                                                unsigned char *smem, int tid, int wc0, int ws0,
@@ -393,6 +427,10 @@ struct GemmCoreDMA {
         constexpr int CP = Cfg::CPR / 2;
         const int KT = K / Cfg::BK;
         if (KT == 0) return;
+        if constexpr (!Cfg::PIPE) {
+            run_simple(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
+            return;
+        }
         // wave index as a scalar: the DMA's LDS base (M0) is then computed on
         // the scalar unit
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -450,6 +488,46 @@ template <class DT, class Cfg>
 struct CoreSel<DT, Cfg, 0> {
     typedef GemmCore<DT, Cfg> type;
     static constexpr int SMEM = 2 * Cfg::STAGE_BYTES;
+};
+
+// ------------------------------------------------- staged block store ----
+// A lane holds 16-byte pieces of 32 different output rows (the MFMA
+// accumulator layout), so a direct store writes 32 bytes per row per
+// instruction.  Instead the wave writes its 32-row x WC-channel block to a
+// private LDS area (16-byte chunks XOR-swizzled by the row's low 4 bits:
+// conflict-free both ways for rows of 64..256 channels) and reads it back
+// row by row, so each store instruction writes WC*4 contiguous bytes per row.
+// value(tc, q) gives the lane's 4 channels 32*tc + 8*q + 4*h .. +3 of its row.
+template <int WC>
+struct BlockStore {
+    static_assert(WC >= 64 && WC <= 256, "block rows of 64..256 channels");
+    static constexpr int BYTES = 32 * WC * 4;
+    static constexpr int CPRW = WC / 4;   // 16-byte chunks per block row
+    static constexpr int RPI = 64 / CPRW; // block rows per store instruction
+    template <class F>
+    static __device__ __forceinline__ void store(unsigned char *blk, int lane, F &&value,
+                                                 float *__restrict__ out, int N, int M,
+                                                 int row0, int col0) {
+        const int lr = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int tc = 0; tc < WC / 32; ++tc)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int chunk = 8 * tc + 2 * q + h;
+                *reinterpret_cast<f32x4 *>(blk + lr * (CPRW * 16) + 16 * (chunk ^ (lr & 15))) =
+                    value(tc, q);
+            }
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int row = RPI * i + lane / CPRW;
+            const int chunk = lane % CPRW;
+            const f32x4 y = *reinterpret_cast<const f32x4 *>(blk + row * (CPRW * 16) +
+                                                             16 * (chunk ^ (row & 15)));
+            const int m = row0 + row;
+            const int c = col0 + 4 * chunk;
+            if (m < M && c < N) *reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + c) = y;
+        }
+    }
 };
 
 // ------------------------------------------------------ tile schedule ----

@@ -135,15 +135,10 @@ void lgn_fused_kernel(
     };
     // ---- normalise, affine, store ----
     //   y = (u - mean) * rstd * gamma + beta = fma(fma(u, rstd, -mean*rstd), gamma, beta)
-    // A lane holds 32-byte pieces of 32 different rows, so the wave first
-    // writes its 32 x WC block to a private LDS area (16-byte chunks XOR-
-    // swizzled by the row's low 4 bits: conflict-free both ways for rows of
-    // 64..256 channels) and reads it back row by row; each store instruction
-    // then writes WC*4 contiguous bytes per row.  When the blocks of all waves
-    // do not fit in the ring, store directly.
-    constexpr int BLK_BYTES = 32 * Cfg::WC * 4;
-    constexpr bool STAGED =
-        (Cfg::NT / 64) * BLK_BYTES <= Sel::SMEM && Cfg::WC >= 64 && Cfg::WC <= 256;
+    // Stores go through the wave's LDS block (whole row segments per
+    // instruction) when the blocks of all waves fit in the ring, else direct.
+    constexpr bool STAGED = Cfg::WC >= 64 && Cfg::WC <= 256 &&
+                            (Cfg::NT / 64) * (32 * Cfg::WC * 4) <= Sel::SMEM;
     auto normalise = [&](int ts, int tc, int q, const float *rstd, const float *nmr) {
         const int ct = wc0 + 32 * tc + 8 * q + 4 * h;
         const int s = (tc * 16 + 4 * q) / NLOC;
@@ -158,27 +153,10 @@ void lgn_fused_kernel(
     };
     auto finish = [&](int ts, const float *rstd, const float *nmr) {
         if constexpr (STAGED) {
-            constexpr int CPRW = Cfg::WC / 4;   // 16-byte chunks per block row
-            constexpr int RPI = 64 / CPRW;      // block rows per store instruction
-            unsigned char *blk = smem + wave * BLK_BYTES;
-#pragma unroll
-            for (int tc = 0; tc < TC; ++tc)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int chunk = 8 * tc + 2 * q + h;
-                    *reinterpret_cast<f32x4 *>(blk + lr * (CPRW * 16) + 16 * (chunk ^ (lr & 15))) =
-                        normalise(ts, tc, q, rstd, nmr);
-                }
-#pragma unroll
-            for (int i = 0; i < 32 / RPI; ++i) {
-                const int row = RPI * i + lane / CPRW;
-                const int chunk = lane % CPRW;
-                const f32x4 y = *reinterpret_cast<const f32x4 *>(blk + row * (CPRW * 16) +
-                                                                 16 * (chunk ^ (row & 15)));
-                const int m = m0 + ws0 + 32 * ts + row;
-                const int c = n0 + wc0 + 4 * chunk;
-                if (m < M && c < N) *reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + c) = y;
-            }
+            typedef BlockStore<Cfg::WC> BS_;
+            BS_::store(smem + wave * BS_::BYTES, lane,
+                       [&](int tc, int q) { return normalise(ts, tc, q, rstd, nmr); }, out, N, M,
+                       m0 + ws0 + 32 * ts, n0 + wc0);
         } else {
             const int m = m0 + ws0 + 32 * ts + lr;
 #pragma unroll

@@ -15,7 +15,8 @@ namespace lgn {
 //   CG == 128 : 256 x 128, 4 x 1 waves of 64 x 128, ring of 3
 //   CG == 256 : 128 x 256, 2 x 2 waves of 64 x 128 (2 waves per group), ring of 3
 //   CG == 512 :  64 x 512, 1 x 4 waves of 64 x 128 (4 waves per group), ring of 3
-//   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128 (8 waves per group), ring of 2
+//   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128 (8 waves per group), ring of 2,
+//                simple schedule (fragments read right before their MFMAs)
 // and register-staged tiles for any other K.
 template <class DT, class Cfg, int CG, int RING>
 hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
@@ -62,7 +63,7 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
     typedef TileCfg<DT, 256, 128, 4, 1, 64, 2> F128;
     typedef TileCfg<DT, 128, 256, 2, 2, 64> F256;
     typedef TileCfg<DT, 64, 512, 1, 4, 64> F512;
-    typedef TileCfg<DT, 64, 1024, 1, 8, 64> F1024;
+    typedef TileCfg<DT, 64, 1024, 1, 8, 64, 1, 0> F1024;   // simple schedule
     const int cg = N / G;
 #define LGN_CASE(C, FAST, RING, SLOW)                                                            \
     case C:                                                                                     \

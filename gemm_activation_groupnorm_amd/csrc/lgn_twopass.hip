@@ -18,15 +18,17 @@ static hipError_t launch_gemm_bias_cfg(const typename dt_traits<DT>::storage *x,
                          dim3(Cfg::NT), stream, x, W, b_lin, M, K, N, z, tiles_m, tiles_n);
 }
 
-// Same tiles as the fused kernel for narrow groups: the LDS DMA ring when K
-// is a multiple of its stage depth, else the register-staged core.
+// 256 x 128 tiles of 4 waves (128 x 64 each): the LDS DMA ring when K is a
+// multiple of its stage depth, else the register-staged core.
 template <class DT>
 static hipError_t launch_gemm_bias(const typename dt_traits<DT>::storage *x,
                                    const typename dt_traits<DT>::storage *W, const float *b_lin,
                                    int M, int K, int N, float *z, hipStream_t stream) {
     typedef TileCfg<DT, 256, 128, 2, 2, 64, 2> Fast;
     typedef TileCfg<DT, 128, 128, 2, 2, 128, 2> Slow;
-    if (K % Fast::BK == 0) return launch_gemm_bias_cfg<DT, Fast, 3>(x, W, b_lin, M, K, N, z, stream);
+    constexpr int RING = 3;
+    if (K % Fast::BK == 0)
+        return launch_gemm_bias_cfg<DT, Fast, RING>(x, W, b_lin, M, K, N, z, stream);
     return launch_gemm_bias_cfg<DT, Slow, 0>(x, W, b_lin, M, K, N, z, stream);
 }
 

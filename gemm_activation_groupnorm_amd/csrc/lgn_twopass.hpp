@@ -47,20 +47,37 @@ void lgn_gemm_bias_kernel(
         }
     Sel::type::run(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
 
+    constexpr bool STAGED = Cfg::WC >= 64 && Cfg::WC <= 256 &&
+                            (Cfg::NT / 64) * (32 * Cfg::WC * 4) <= Sel::SMEM;
+    if constexpr (STAGED) {
+        typedef BlockStore<Cfg::WC> BS_;
+        __syncthreads();   // all waves are done with the ring
 #pragma unroll
-    for (int tc = 0; tc < Cfg::TC; ++tc) {
+        for (int ts = 0; ts < Cfg::TS; ++ts)
+            BS_::store(smem + wave * BS_::BYTES, lane,
+                       [&](int tc, int q) {
+                           f32x4 v;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = n0 + wc0 + 32 * tc + 8 * q + 4 * h;
-            if (c >= N) continue;
+                           for (int j = 0; j < 4; ++j) v[j] = acc[ts][tc][4 * q + j];
+                           return v;
+                       },
+                       z, N, M, m0 + ws0 + 32 * ts, n0 + wc0);
+    } else {
 #pragma unroll
-            for (int ts = 0; ts < Cfg::TS; ++ts) {
-                const int m = m0 + ws0 + 32 * ts + lr;
-                if (m >= M) continue;
-                f32x4 v;
+        for (int tc = 0; tc < Cfg::TC; ++tc) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = acc[ts][tc][4 * q + j];
-                *reinterpret_cast<f32x4 *>(z + (size_t)m * (size_t)N + c) = v;
+            for (int q = 0; q < 4; ++q) {
+                const int c = n0 + wc0 + 32 * tc + 8 * q + 4 * h;
+                if (c >= N) continue;
+#pragma unroll
+                for (int ts = 0; ts < Cfg::TS; ++ts) {
+                    const int m = m0 + ws0 + 32 * ts + lr;
+                    if (m >= M) continue;
+                    f32x4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = acc[ts][tc][4 * q + j];
+                    *reinterpret_cast<f32x4 *>(z + (size_t)m * (size_t)N + c) = v;
+                }
             }
         }
     }
