@@ -138,6 +138,42 @@ class Runner:
         return float(np.max(np.abs(y - ref))), len(rows)
 
 
+def torch_context(w):
+    """Context only: torch's linear (vendor GEMM, output in the input type) and
+    the unfused torch pipeline (linear, SiLU, add, group_norm) on random
+    inputs of the workload's shape and type.  Not part of the product."""
+    import torch
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    x = torch.randn(w.M, w.K, device="cuda", dtype=dt)
+    W = torch.randn(w.N, w.K, device="cuda", dtype=dt)
+    vec = [torch.randn(w.N, device="cuda") for _ in range(4)]
+
+    def t(f, n=10):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def pipe():
+        z = torch.nn.functional.linear(x, W).float() + vec[0]
+        u = torch.nn.functional.silu(z) + vec[1]
+        return torch.nn.functional.group_norm(u, w.G, vec[2], vec[3], w.eps)
+
+    g_ms = t(lambda: torch.nn.functional.linear(x, W))
+    p_ms = t(pipe)
+    del x, W
+    torch.cuda.empty_cache()
+    return {"torch_linear_ms": round(g_ms, 4), "torch_linear_tflops": round(w.flops / g_ms / 1e9, 1),
+            "torch_unfused_pipeline_ms": round(p_ms, 4),
+            "note": "context only: torch linear = vendor GEMM with output in the input type"}
+
+
 def cpu_baseline(w, inp, seconds: float):
     import oracle
     x, W = inp["x"], inp["W"]
@@ -172,6 +208,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (bf16, wide group, two-pass)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--torch-context", action="store_true",
+                    help="also time, for context only, torch's linear (vendor GEMM) and the "
+                         "unfused torch pipeline on the same workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the forward, run 5 plain device copies of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -268,6 +307,9 @@ def main():
             del re
             torch.cuda.empty_cache()
         res["extra"] = extra
+
+    if args.torch_context:
+        res["torch_context"] = torch_context(w)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
