@@ -106,13 +106,21 @@ class Runner:
             ws = self.ws
             self.launch = lambda: lgn.check(fn(*args, ws, nb, stream=s))
 
-    def time(self, steps: int, warmup: int):
+    def time(self, steps: int, warmup: int, min_warm_ms: float = 0.0):
         """Wall time of `steps` back-to-back launches and the mean launch
-        duration from one HIP event pair on the launch stream around them."""
+        duration from one HIP event pair on the launch stream around them.
+        `warmup` untimed launches first; with min_warm_ms > 0 the warm-up goes
+        on until that much GPU time has passed (the clocks ramp up under load
+        over tens of milliseconds)."""
         import torch
+        t_warm = time.perf_counter()
         for _ in range(warmup):
             self.launch()
         torch.cuda.synchronize()
+        while (time.perf_counter() - t_warm) * 1e3 < min_warm_ms:
+            for _ in range(max(1, warmup)):
+                self.launch()
+            torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -201,7 +209,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", default="fused", choices=["fused", "twopass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -294,7 +302,7 @@ def main():
                 continue
             we = get_workload(name)
             re = Runner(we, variant)
-            wl, km_mean = re.time(20, 5)
+            wl, km_mean = re.time(50, 5, min_warm_ms=100.0)
             ach = we.flops / (km_mean * 1e-3) / 1e12
             e2, _ = re.check_rows(4)
             eprint("[bench] %s/%s: kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f), err %.2e"

@@ -45,10 +45,15 @@ template <> struct dt_traits<bf16_t> {
 // BS samples x BC channels per workgroup; WAVES_S x WAVES_C waves; each wave
 // owns WS x WC = (32*TS) x (32*TC) of the tile.  ROWB bytes of K per LDS row.
 // OCC = waves per SIMD the kernel must fit (register budget 512/OCC per
-// lane, accumulators included).  PIPE: the LDS DMA core reads the next
-// chunk pair's fragments under the current MFMAs (1) or reads each chunk
-// pair's fragments right before its MFMAs (0).  EARLY (PIPE only) = sample
-// tiles whose MFMAs are issued before those reads (0: reads first).
+// lane, accumulators included).  PIPE selects the LDS DMA core's schedule:
+//   0: each chunk pair's fragments are read right before its MFMAs;
+//   1: the next chunk pair's fragments are read under the current MFMAs, one
+//      barrier at the end of each stage;
+//   2: as 1, with the barrier before the stage's last chunk pair, so that the
+//      next stage's first reads hide under that whole chunk pair (needs a
+//      ring of at least 3 stages and an even number of chunk pairs).
+// EARLY (PIPE >= 1) = sample tiles whose MFMAs are issued before those reads
+// (0: reads first).
 template <class DT, int BS_, int BC_, int WAVES_S_, int WAVES_C_, int ROWB_, int OCC_ = 1,
           int PIPE_ = 1, int EARLY_ = 1>
 struct TileCfg {
@@ -56,6 +61,7 @@ struct TileCfg {
     static constexpr int ROWB = ROWB_;
     static constexpr int OCC = OCC_;
     static constexpr bool PIPE = PIPE_ != 0;
+    static constexpr int SCHED = PIPE_;
     static constexpr int EARLY = EARLY_;
     static constexpr int NT = 64 * WAVES_S * WAVES_C;
     static constexpr int WS = BS / WAVES_S, WC = BC / WAVES_C;
@@ -243,15 +249,12 @@ struct GemmCore {
 // chunk p of LDS row r fetches logical chunk p ^ f(r).  Rows past M or N are
 // clamped to the last row (their results are never stored).
 //
-// Synchronisation per stage kt (one barrier):
-//   s_waitcnt vmcnt(<loads issued after stage kt>)  -- my part of stage kt landed
-//   s_barrier                                       -- everyone's part landed, and
-//                                                      everyone finished stage kt-1
-//   issue stage kt+STAGES-1 into the ring slot of stage kt-1
-//   ds_read + MFMA on stage kt
-// Every wave's LDS reads of a stage complete before its next barrier (the
-// MFMAs that consume them wait on lgkmcnt), so a slot is refilled only after
-// all waves are done with it.
+// Synchronisation, one barrier per stage.  Before it a wave waits (vmcnt) for
+// its own DMA share of the stage about to be read and has consumed, with its
+// MFMAs, every fragment of the slot about to be refilled; after it, the whole
+// stage is visible and the slot is free for every wave.  The schedules differ
+// in where the barrier sits (end of stage, or before its last chunk pair) and
+// so in how many stages the refill runs ahead.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
@@ -380,6 +383,74 @@ struct GemmCoreDMA {
         }
     }
 
+    // Schedule 2, chunk pair CPI of stage kt.  The barrier sits before the
+    // last chunk pair: by then this wave's MFMAs have consumed every fragment
+    // of stage kt-1 (so, past the barrier, that slot is free for every wave)
+    // and, after the vmcnt wait, its DMA share of stage kt+1 has landed (so,
+    // past the barrier, all of stage kt+1 is visible).  The last chunk pair
+    // then reads stage kt+1's first fragments and refills the slot of stage
+    // kt-1 with stage kt+STAGES-1 under its own MFMAs.  No LDS read is waited
+    // for at the barrier: the reads in flight there are of stage kt.
+    template <int CPI>
+    static __device__ __forceinline__ void mb_step(unsigned char *smem, int kt, int KT, int wave,
+                                                   int wc0, int ws0, int lr, int h,
+                                                   const unsigned char *const (&src)[BPW],
+                                                   Frags &cur, Frags &nxt,
+                                                   f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+        typedef GemmCore<DT, Cfg> C;
+        constexpr int CP = Cfg::CPR / 2;
+        C::template mfma_block<0, EARLY>(cur.a, cur.b, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (CPI + 1 < CP) {
+            C::load_frags(smem + (kt % STAGES) * Cfg::STAGE_BYTES, CPI + 1, wc0, ws0, lr, h,
+                          nxt.a, nxt.b);
+            __builtin_amdgcn_sched_barrier(0);
+            C::template mfma_block<EARLY, Cfg::TS>(cur.a, cur.b, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (CPI + 2 == CP) {
+                wait_vmcnt<(STAGES - 3) * BPW>();
+                block_barrier();
+            }
+            mb_step<CPI + 1>(smem, kt, KT, wave, wc0, ws0, lr, h, src, nxt, cur, acc);
+        } else {
+            C::load_frags(smem + ((kt + 1) % STAGES) * Cfg::STAGE_BYTES, 0, wc0, ws0, lr, h,
+                          nxt.a, nxt.b);
+            const int ns = kt + STAGES - 1;
+            issue(smem, ns % STAGES, wave, ns < KT ? ns : KT - 1, src);
+            __builtin_amdgcn_sched_barrier(0);
+            C::template mfma_block<EARLY, Cfg::TS>(cur.a, cur.b, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // Schedule 2 main loop.  The prologue fills STAGES-1 slots; iteration kt
+    // issues stage kt+STAGES-1 (clamped to the last stage past the end, into
+    // a slot no later stage reads), so before the barrier of stage kt the
+    // loads of stages kt+2 .. kt+STAGES-2 may still be in flight.  The reads
+    // of "stage KT" in the last iteration fetch a slot nobody uses.
+    static __device__ __forceinline__ void run_midbar(const T *__restrict__ x,
+                                                      const T *__restrict__ W, int M, int N, int K,
+                                                      int m0, int n0, unsigned char *smem, int tid,
+                                                      int wc0, int ws0, int lr, int h,
+                                                      f32x16 (&acc)[Cfg::TS][Cfg::TC]) {
+        static_assert(STAGES >= 3, "schedule 2 refills the slot of the previous stage");
+        static_assert(Cfg::CPR / 2 >= 2 && (Cfg::CPR / 2) % 2 == 0,
+                      "schedule 2: an even number of chunk pairs per stage");
+        const int KT = K / Cfg::BK;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+        const unsigned char *src[BPW];
+        setup(x, W, M, N, K, m0, n0, wave, lane, src);
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) issue(smem, s, wave, s < KT ? s : KT - 1, src);
+        wait_vmcnt<(STAGES - 2) * BPW>();
+        block_barrier();
+        Frags fa, fb;
+        GemmCore<DT, Cfg>::load_frags(smem, 0, wc0, ws0, lr, h, fa.a, fa.b);
+        for (int kt = 0; kt < KT; ++kt)
+            mb_step<0>(smem, kt, KT, wave, wc0, ws0, lr, h, src, fa, fb, acc);
+        wait_vmcnt<0>();   // no DMA may land in LDS after the main loop
+    }
+
     template <bool HANDOVER, bool ISSUE, int AFTER>
     static __device__ __forceinline__ void stage_body(unsigned char *smem, int kt, int KT, int wave,
                                                       int wc0, int ws0, int lr, int h,
@@ -429,6 +500,9 @@ struct GemmCoreDMA {
         if (KT == 0) return;
         if constexpr (!Cfg::PIPE) {
             run_simple(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
+            return;
+        } else if constexpr (Cfg::SCHED == 2) {
+            run_midbar(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
             return;
         }
         // wave index as a scalar: the DMA's LDS base (M0) is then computed on

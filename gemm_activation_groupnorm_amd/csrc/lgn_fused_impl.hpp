@@ -11,7 +11,8 @@ namespace lgn {
 
 // Tiles per channel-per-group count CG, for K a multiple of the stage depth
 // (LDS DMA ring) -- BS samples x BC channels, waves along samples x channels:
-//   CG <= 64  : 256 x 256, 2 x 4 waves of 128 x 64, ring of 4 (bf16) / 3 (fp32)
+//   CG <= 64  : 256 x 256, 2 x 4 waves of 128 x 64; bf16: ring of 4 with the
+//               mid-stage barrier schedule; fp32: ring of 3
 //   CG == 128 : 256 x 128, 4 x 1 waves of 64 x 128, ring of 3
 //   CG == 256 : 128 x 256, 2 x 2 waves of 64 x 128 (2 waves per group), ring of 3
 //   CG == 512 :  64 x 512, 1 x 4 waves of 64 x 128 (4 waves per group), ring of 3
@@ -58,7 +59,11 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
     typedef TileCfg<DT, 64, 512, 1, 4, 64> S512;
     typedef TileCfg<DT, 64, 1024, 1, 8, 32> S1024;
     // LDS DMA ring tiles (K % BK == 0)
-    typedef TileCfg<DT, 256, 256, 2, 4, 64, 2> F64;
+    // fp32: end-of-stage barrier, ring of 3; bf16 (16x shorter stages):
+    // mid-stage barrier, ring of 4, two sample tiles of MFMAs ahead of reads
+    typedef typename std::conditional<std::is_same<DT, bf16_t>::value,
+                                      TileCfg<DT, 256, 256, 2, 4, 64, 2, 2, 2>,
+                                      TileCfg<DT, 256, 256, 2, 4, 64, 2>>::type F64;
     constexpr int R64 = std::is_same<DT, bf16_t>::value ? 4 : 3;
     typedef TileCfg<DT, 256, 128, 4, 1, 64, 2> F128;
     typedef TileCfg<DT, 128, 256, 2, 2, 64> F256;
