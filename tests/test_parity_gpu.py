@@ -128,6 +128,33 @@ def test_full_size_workloads_sampled(wi, variant):
         assert float(var.max()) < 1.0 + 2e-3 and float(var.min()) > 0.99
 
 
+# ---- an output past 2^31 elements: 64-bit row offsets in every store ----
+
+@pytest.mark.parametrize("variant,dtype", [("fused", "f32"), ("fused", "bf16"),
+                                           ("twopass", "f32")])
+def test_output_beyond_2p31_elements(variant, dtype):
+    M, K, N, G = (1 << 19) + 77, 32, 4096, 64   # M*N = 2^31 + 315392
+    assert M * N > 2 ** 31
+    log("case M=%d K=%d N=%d G=%d dtype=%s variant=%s (8.6 GB output)" % (M, K, N, G, dtype,
+                                                                         variant))
+    inp = case(M, K, N, G, 31, dtype)
+    dev = to_device(inp, dtype)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    # the two-pass path runs in place (workspace = out) to halve the footprint
+    y = run(dev, M, K, N, G, 1e-5, dtype, variant, out=out, ws=out if variant == "twopass" else None)
+    torch.cuda.synchronize()
+    first_high = (1 << 31) // N   # first row whose elements sit past 2^31
+    rows = np.unique(np.concatenate([[0, first_high - 1, first_high, first_high + 1, M - 1],
+                                     sample_rows(M, 16, seed=31)]))
+    err = max_err(y[torch.from_numpy(rows).cuda()].cpu().numpy(),
+                  oracle_rows(inp, G, 1e-5, rows))
+    log("  sampled-row max abs err %.3e" % err)
+    assert err <= TOL[dtype]
+    assert bool(torch.isfinite(y[first_high - 8:]).all())
+    del y, out, dev
+    torch.cuda.empty_cache()
+
+
 # ---- determinism, row independence, in place, streams, bounds ----
 
 @pytest.mark.parametrize("variant", VARIANTS)
