@@ -15,8 +15,16 @@ statement and the passages fixing the forward order):
         mu  = mean(u[m, gC:(g+1)C]),  var = population variance
     y = (u - mu) / sqrt(var + eps) * gamma + beta
 
+Second method (POPCORNBENCH transcript "Kimi-K2.6 l2_p64", problem statement),
+one scalar per row:
+
+    z = x . W^T + b
+    l = log(sum_n exp(z[n]))         (row maximum first, then the shifted sum)
+    out = gelu(gelu(leaky(leaky(l))))    leaky slope 0.01, exact gelu v*Phi(v)
+
 All arithmetic is IEEE double in plain C (``lgn_oracle.c``), sequential sums,
-no FMA contraction.  Pins: ``tests/test_oracle_pins.py``.
+no FMA contraction.  Pins: ``tests/test_oracle_pins.py`` and
+``tests/test_lse_oracle_pins.py``.
 """
 from __future__ import annotations
 
@@ -68,6 +76,18 @@ def _load():
             lib.oracle_lgn_forward.argtypes = [dp, dp, dp, dp, dp, dp, L, L, L, L,
                                                ctypes.c_double, dp]
             lib.oracle_lgn_forward.restype = ctypes.c_int
+            lib.oracle_logsumexp.argtypes = [dp, L]
+            lib.oracle_logsumexp.restype = ctypes.c_double
+            lib.oracle_leaky_relu.argtypes = [ctypes.c_double]
+            lib.oracle_leaky_relu.restype = ctypes.c_double
+            lib.oracle_gelu.argtypes = [ctypes.c_double]
+            lib.oracle_gelu.restype = ctypes.c_double
+            lib.oracle_logsumexp_rows.argtypes = [dp, L, L, dp]
+            lib.oracle_logsumexp_rows.restype = None
+            lib.oracle_activation_array.argtypes = [dp, dp, L, ctypes.c_int]
+            lib.oracle_activation_array.restype = None
+            lib.oracle_linear_lse_forward.argtypes = [dp, dp, dp, L, L, L, dp, dp]
+            lib.oracle_linear_lse_forward.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -135,6 +155,51 @@ def lgn_forward(x, W, b_lin, b_add, gamma, beta, G: int, eps: float) -> np.ndarr
     if rc != 0:
         raise ValueError("oracle_lgn_forward failed with code %d" % rc)
     return y
+
+
+# ---- second method: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 ----
+# (POPCORNBENCH transcript "Kimi-K2.6 l2_p64", problem statement)
+
+def logsumexp_rows(z) -> np.ndarray:
+    """log(sum_n exp(z[m, n])) of every row of z [M, N] (N >= 1)."""
+    z = _f64(z)
+    M, N = z.shape
+    assert N >= 1
+    out = np.empty(M, dtype=np.float64)
+    _load().oracle_logsumexp_rows(_ptr(z), M, N, _ptr(out))
+    return out
+
+
+def _activation(v, which: int) -> np.ndarray:
+    v = _f64(v)
+    out = np.empty_like(v)
+    _load().oracle_activation_array(_ptr(v), _ptr(out), v.size, which)
+    return out
+
+
+def leaky_relu(v) -> np.ndarray:
+    """LeakyReLU with negative slope 0.01, elementwise."""
+    return _activation(v, 0)
+
+
+def gelu(v) -> np.ndarray:
+    """Exact GELU v * Phi(v), elementwise."""
+    return _activation(v, 1)
+
+
+def linear_lse_forward(x, W, b, return_lse: bool = False):
+    """out[m] = gelu(gelu(leaky(leaky(logsumexp(x[m] . W^T + b))))), fp64."""
+    x, W, b = _f64(x), _f64(W), _f64(b)
+    M, K = x.shape
+    N = W.shape[0]
+    assert W.shape == (N, K) and b.shape == (N,)
+    out = np.empty(M, dtype=np.float64)
+    lse = np.empty(M, dtype=np.float64)
+    rc = _load().oracle_linear_lse_forward(_ptr(x), _ptr(W), _ptr(b), M, K, N, _ptr(out),
+                                           _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_linear_lse_forward failed with code %d" % rc)
+    return (out, lse) if return_lse else out
 
 
 def num_threads() -> int:

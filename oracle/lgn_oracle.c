@@ -3,6 +3,10 @@
  *
  *     y = GroupNorm_G( Swish(x . W^T + b_lin) + b_add ) * gamma + beta
  *
+ * and for the second method, one scalar per row,
+ *
+ *     out = GELU(GELU(LeakyReLU(LeakyReLU(logsumexp_n(x . W^T + b)))))
+ *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
  * header, table or helper with the HIP library and must never be called by
@@ -146,6 +150,87 @@ int oracle_lgn_forward(const double *x, const double *W, const double *b_lin,
                 row[n] = oracle_swish(row[n]) + b_add[n];
             /* steps 4-5: group statistics, normalise, affine */
             groupnorm_row(row, gamma, beta, N, G, eps, yrow, NULL, NULL);
+        }
+        free(row);
+    }
+    return failed ? -2 : 0;
+}
+
+/* ====================================================================== *
+ * Second method: Linear -> logsumexp over the output features -> LeakyReLU
+ * twice -> GELU twice (POPCORNBENCH transcript "Kimi-K2.6 l2_p64", problem
+ * statement: logsumexp over dim 1 with keepdim, negative slope 0.01, and the
+ * exact GELU that the transcript settles on, x * Phi(x) with the normal CDF
+ * Phi written through erf).  One output scalar per row.
+ * ====================================================================== */
+
+/* log(sum_n exp(z[n])) of one row of N >= 1 values, computed the way the
+ * transcript's post-GEMM kernel does: the row maximum first, then the sum of
+ * exp(z[n] - max) in index order, then max + log(sum).                     */
+double oracle_logsumexp(const double *z, long N)
+{
+    double mx = z[0];
+    for (long n = 1; n < N; ++n)
+        if (z[n] > mx) mx = z[n];
+    double s = 0.0;
+    for (long n = 0; n < N; ++n)
+        s += exp(z[n] - mx);
+    return mx + log(s);
+}
+
+/* LeakyReLU with negative slope 0.01. */
+double oracle_leaky_relu(double v)
+{
+    return v > 0.0 ? v : 0.01 * v;
+}
+
+/* Exact GELU: v * Phi(v), Phi(v) = (1 + erf(v / sqrt 2)) / 2. */
+double oracle_gelu(double v)
+{
+    return v * (0.5 * (1.0 + erf(v / sqrt(2.0))));
+}
+
+/* out[m] = logsumexp(z[m][0..N-1]) */
+void oracle_logsumexp_rows(const double *z, long M, long N, double *out)
+{
+    for (long m = 0; m < M; ++m)
+        out[m] = oracle_logsumexp(z + (size_t)m * (size_t)N, N);
+}
+
+/* out[i] = f(in[i]); which = 0 LeakyReLU, 1 GELU */
+void oracle_activation_array(const double *in, double *out, long n, int which)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = which == 0 ? oracle_leaky_relu(in[i]) : oracle_gelu(in[i]);
+}
+
+/* The whole second forward, row by row:
+ *   z = x[m] . W^T + b;  l = logsumexp(z);
+ *   out[m] = gelu(gelu(leaky(leaky(l))))
+ * lse_out (optional) receives l.  Returns 0, -1 on bad arguments, -2 if a
+ * row buffer could not be allocated.                                        */
+int oracle_linear_lse_forward(const double *x, const double *W, const double *b,
+                              long M, long K, long N, double *out, double *lse_out)
+{
+    if (M < 0 || K < 0 || N <= 0)
+        return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *row = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!row) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        long m;
+#pragma omp for schedule(static)
+        for (m = 0; m < M; ++m) {
+            if (!row) continue;
+            linear_row(x + (size_t)m * (size_t)K, W, b, K, N, row);
+            double l = oracle_logsumexp(row, N);
+            double v = oracle_leaky_relu(oracle_leaky_relu(l));
+            out[m] = oracle_gelu(oracle_gelu(v));
+            if (lse_out) lse_out[m] = l;
         }
         free(row);
     }
