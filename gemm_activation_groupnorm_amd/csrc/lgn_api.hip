@@ -105,6 +105,28 @@ lgn_status forward_twopass(const T *x, const T *W, const float *b_lin, const flo
     return from_hip(lgn::launch_gn_epilogue(z, b_add, gamma, beta, M, N, G, eps, out, stream));
 }
 
+template <int DT, class T>
+lgn_status linear_lse(const T *x, const T *W, const float *b, int M, int K, int N, float *out,
+                      void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (M < 0 || K < 0 || N < 1) return LGN_ERR_INVALID_ARG;
+    if (M == 0) return LGN_OK;   // empty batch: nothing is read or written
+    if (!b || !out || !workspace) return LGN_ERR_INVALID_ARG;
+    if (K > 0 && (!x || !W)) return LGN_ERR_INVALID_ARG;
+    if (ws_bytes < lgn_lse_workspace_bytes(M, N)) return LGN_ERR_INVALID_ARG;
+    const int epc = DT == DT_F32 ? 4 : 8;
+    if (K % epc != 0 || N % 4 != 0) return LGN_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(b, 4) || !aligned(out, 4) ||
+        !aligned(workspace, 8))
+        return LGN_ERR_UNSUPPORTED;
+    lgn_status s = check_device();
+    if (s != LGN_OK) return s;
+    if (DT == DT_F32)
+        return from_hip(lgn::launch_linear_lse_f32((const float *)x, (const float *)W, b, M, K,
+                                                   N, out, workspace, stream));
+    return from_hip(lgn::launch_linear_lse_bf16((const uint16_t *)x, (const uint16_t *)W, b, M,
+                                                K, N, out, workspace, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,6 +170,24 @@ lgn_status lgn_forward_twopass_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const 
                                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return forward_twopass<DT_BF16>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
                                     workspace, workspace_bytes, stream);
+}
+
+size_t lgn_lse_workspace_bytes(int M, int N) {
+    if (M <= 0 || N <= 0) return 0;
+    const size_t tiles = ((size_t)N + lgn::kLseTileChannels - 1) / lgn::kLseTileChannels;
+    return (size_t)M * tiles * 2 * sizeof(float);
+}
+
+lgn_status lgn_linear_lse_f32(const float *x, const float *W, const float *b, int M, int K,
+                              int N, float *out, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    return linear_lse<DT_F32>(x, W, b, M, K, N, out, workspace, workspace_bytes, stream);
+}
+
+lgn_status lgn_linear_lse_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float *b, int M,
+                               int K, int N, float *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    return linear_lse<DT_BF16>(x, W, b, M, K, N, out, workspace, workspace_bytes, stream);
 }
 
 const char *lgn_status_string(lgn_status s) {

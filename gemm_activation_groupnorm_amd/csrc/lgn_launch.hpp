@@ -39,6 +39,14 @@ hipError_t launch_fused_bf16(const uint16_t *x, const uint16_t *W, const float *
                              const float *b_add, const float *gamma, const float *beta, int M,
                              int K, int N, int G, float eps, float *out, hipStream_t stream);
 
+// Linear -> logsumexp -> LeakyReLU x2 -> GELU x2.  The workspace holds one
+// (max, sum) float pair per row and per tile of this many channels.
+constexpr int kLseTileChannels = 256;
+hipError_t launch_linear_lse_f32(const float *x, const float *W, const float *b, int M, int K,
+                                 int N, float *out, void *workspace, hipStream_t stream);
+hipError_t launch_linear_lse_bf16(const uint16_t *x, const uint16_t *W, const float *b, int M,
+                                  int K, int N, float *out, void *workspace, hipStream_t stream);
+
 hipError_t launch_gemm_bias_f32(const float *x, const float *W, const float *b_lin, int M,
                                 int K, int N, float *z, hipStream_t stream);
 hipError_t launch_gemm_bias_bf16(const uint16_t *x, const uint16_t *W, const float *b_lin,

@@ -62,6 +62,15 @@ WORKLOADS = [
 ]
 
 
+# The second method (Linear -> logsumexp -> LeakyReLU x2 -> GELU x2) at the
+# shape of its transcript: batch 1024, 8192 input and 8192 output features.
+# It uses x, W and b_lin (as the linear bias) of the same draw; G is unused.
+LSE_WORKLOADS = [
+    Workload("m1024_k8192_n8192_lse_f32", 1024, 8192, 8192, 1, "f32", 5),
+    Workload("m1024_k8192_n8192_lse_bf16", 1024, 8192, 8192, 1, "bf16", 6),
+]
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits.
 
@@ -111,7 +120,7 @@ def workload_inputs(w: Workload) -> Dict[str, np.ndarray]:
 def get_workload(name_or_index) -> Workload:
     if isinstance(name_or_index, int):
         return WORKLOADS[name_or_index]
-    for w in WORKLOADS:
+    for w in WORKLOADS + LSE_WORKLOADS:
         if w.name == name_or_index:
             return w
     raise KeyError(name_or_index)

@@ -33,6 +33,9 @@ EXPORTS = (
     "lgn_twopass_workspace_bytes",
     "lgn_forward_twopass_f32",
     "lgn_forward_twopass_bf16",
+    "lgn_lse_workspace_bytes",
+    "lgn_linear_lse_f32",
+    "lgn_linear_lse_bf16",
     "lgn_status_string",
     "lgn_version",
     "lgn_last_hip_error_string",
@@ -66,6 +69,7 @@ def _load():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     fwd = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, vp]
     two = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, vp, sz, vp]
+    lse = [vp, vp, vp, i, i, i, vp, vp, sz, vp]
     for name, args, res in (
         ("lgn_forward_f32", fwd, i),
         ("lgn_forward_bf16", fwd, i),
@@ -73,6 +77,9 @@ def _load():
         ("lgn_twopass_workspace_bytes", [i, i], sz),
         ("lgn_forward_twopass_f32", two, i),
         ("lgn_forward_twopass_bf16", two, i),
+        ("lgn_lse_workspace_bytes", [i, i], sz),
+        ("lgn_linear_lse_f32", lse, i),
+        ("lgn_linear_lse_bf16", lse, i),
         ("lgn_status_string", [i], ctypes.c_char_p),
         ("lgn_version", [], ctypes.c_char_p),
         ("lgn_last_hip_error_string", [], ctypes.c_char_p),
@@ -148,6 +155,22 @@ def lgn_forward_twopass_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, o
                                          _ptr(beta, "f32"), M, K, N, G, eps, _ptr(out, "f32"),
                                          _ptr(workspace, None), workspace_bytes,
                                          _stream(stream))
+
+
+def lgn_lse_workspace_bytes(M: int, N: int) -> int:
+    return _lib.lgn_lse_workspace_bytes(M, N)
+
+
+def lgn_linear_lse_f32(x, W, b, M, K, N, out, workspace, workspace_bytes, stream=None) -> int:
+    return _lib.lgn_linear_lse_f32(_ptr(x, "f32"), _ptr(W, "f32"), _ptr(b, "f32"), M, K, N,
+                                   _ptr(out, "f32"), _ptr(workspace, None), workspace_bytes,
+                                   _stream(stream))
+
+
+def lgn_linear_lse_bf16(x, W, b, M, K, N, out, workspace, workspace_bytes, stream=None) -> int:
+    return _lib.lgn_linear_lse_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b, "f32"), M, K, N,
+                                    _ptr(out, "f32"), _ptr(workspace, None), workspace_bytes,
+                                    _stream(stream))
 
 
 def lgn_status_string(status: int) -> str:

@@ -1,6 +1,7 @@
 /*
  * lgn.h -- C ABI of liblgn.so: fused Linear -> Swish -> +bias -> GroupNorm
- * on AMD Instinct MI355X (gfx950).
+ * on AMD Instinct MI355X (gfx950), and Linear -> logsumexp -> LeakyReLU x2 ->
+ * GELU x2 (declared at the end).
  *
  * The operation (POPCORNBENCH transcript "Kimi-K2.6 l2_p37", problem
  * statement and the passages fixing the forward order):
@@ -55,7 +56,7 @@ enum {
 /* Raw bfloat16 bits: the upper 16 bits of an IEEE binary32. */
 typedef uint16_t lgn_bf16;
 
-/* Shape rules common to every entry point:
+/* Shape rules common to the GroupNorm entry points:
  *   M >= 0 (M == 0 launches nothing and returns LGN_OK), K >= 0, N >= 1,
  *   G >= 1, N % G == 0, eps > 0 and finite.
  *   Pointers may be NULL only when the array they address is empty
@@ -109,6 +110,36 @@ lgn_status lgn_forward_twopass_bf16(const lgn_bf16 *x, const lgn_bf16 *W,
                                     int M, int K, int N, int G, float eps,
                                     float *out, void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/* ---- Second method: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 ----
+ * (POPCORNBENCH transcript "Kimi-K2.6 l2_p64", problem statement: logsumexp
+ * over the output features of each row, LeakyReLU with negative slope 0.01
+ * applied twice, then the exact GELU v * Phi(v), Phi the standard normal CDF,
+ * applied twice.)  One fp32 scalar per row:
+ *
+ *   z[m,n]  = sum_k x[m,k] * W[n,k] + b[n]              nn.Linear, W is [N,K]
+ *   l[m]    = log(sum_n exp(z[m,n]))
+ *   out[m]  = gelu(gelu(leaky(leaky(l[m]))))
+ *
+ * Layouts: x [M,K], W [N,K] dense row-major; b [N] fp32; out [M] fp32.
+ * Kernel 1 runs the MFMA GEMM on 256-channel tiles and writes, per row and
+ * tile, the pair (max, sum of exp(z - max)) into `workspace`; kernel 2 merges
+ * a row's pairs in tile order and applies the activations.  `workspace` must
+ * hold lgn_lse_workspace_bytes(M, N) bytes (8 per row per 256-channel tile),
+ * be 8-byte aligned and overlap nothing else; its contents on entry do not
+ * matter.  Shape rules: M >= 0 (M == 0 is a no-op), K >= 0, N >= 1; x and W
+ * 16-byte aligned, N % 4 == 0, K % 4 == 0 (fp32) or K % 8 == 0 (bf16), else
+ * LGN_ERR_UNSUPPORTED.  Results are bitwise reproducible. */
+size_t lgn_lse_workspace_bytes(int M, int N);
+
+lgn_status lgn_linear_lse_f32(const float *x, const float *W, const float *b,
+                              int M, int K, int N, float *out,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Same with x and W in bfloat16 (bf16 MFMA, fp32 accumulate). */
+lgn_status lgn_linear_lse_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float *b,
+                               int M, int K, int N, float *out,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *lgn_status_string(lgn_status s);

@@ -119,3 +119,49 @@ def test_binding_rejects_non_contiguous_tensor():
         lgn._ptr(t, "f32")
     with pytest.raises(ValueError):
         lgn._ptr(torch.zeros(4, dtype=torch.float64), "f32")
+
+
+# ---- Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 ----
+
+LSE_FNS = [lgn.lgn_linear_lse_f32, lgn.lgn_linear_lse_bf16]
+LSE_GOOD = dict(M=64, K=32, N=300)
+
+
+def _call_lse(fn, **kw):
+    a = dict(x=A, W=A, b=A, out=A, ws=A, ws_bytes=1 << 40, **LSE_GOOD)
+    a.update(kw)
+    return fn(a["x"], a["W"], a["b"], a["M"], a["K"], a["N"], a["out"], a["ws"], a["ws_bytes"],
+              stream=0)
+
+
+def test_lse_workspace_bytes():
+    # one (max, sum) float pair per row and per 256-channel tile
+    assert lgn.lgn_lse_workspace_bytes(1024, 8192) == 1024 * 32 * 8
+    assert lgn.lgn_lse_workspace_bytes(3, 257) == 3 * 2 * 8
+    assert lgn.lgn_lse_workspace_bytes(3, 256) == 3 * 1 * 8
+    assert lgn.lgn_lse_workspace_bytes(0, 16) == 0
+    assert lgn.lgn_lse_workspace_bytes(5, 0) == 0
+
+
+LSE_INVALID = [dict(M=-1), dict(K=-1), dict(N=0), dict(b=None), dict(out=None), dict(ws=None),
+               dict(x=None), dict(W=None), dict(ws_bytes=lgn.lgn_lse_workspace_bytes(64, 300) - 1)]
+LSE_UNSUPPORTED = [dict(K=6), dict(N=302), dict(x=A + 4), dict(W=A + 8), dict(b=A + 2),
+                   dict(out=A + 2), dict(ws=A + 4)]
+
+
+@pytest.mark.parametrize("fn", LSE_FNS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("bad", LSE_INVALID, ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_lse_invalid_arguments(fn, bad):
+    assert _call_lse(fn, **bad) == lgn.LGN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", LSE_FNS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("bad", LSE_UNSUPPORTED,
+                         ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_lse_unsupported_shapes(fn, bad):
+    assert _call_lse(fn, **bad) == lgn.LGN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", LSE_FNS, ids=lambda f: f.__name__)
+def test_lse_empty_batch_is_a_no_op(fn):
+    assert _call_lse(fn, M=0, x=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK
