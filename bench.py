@@ -86,8 +86,13 @@ class Runner:
         else:
             for k in ("x", "W"):
                 self.d[k] = torch.from_numpy(self.inp[k]).to(dev)
-        self.out = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
         self.ws = None
+        if variant == "lse":
+            self.out = torch.empty(w.M, dtype=torch.float32, device=dev)
+            nb_lse = lgn.lgn_lse_workspace_bytes(w.M, w.N)
+            self.ws = torch.empty(max(1, nb_lse // 4), dtype=torch.float32, device=dev)
+        else:
+            self.out = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
         if variant == "twopass":
             self.ws = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
@@ -100,6 +105,11 @@ class Runner:
         if variant == "fused":
             fn = lgn.lgn_forward_f32 if w.dtype == "f32" else lgn.lgn_forward_bf16
             self.launch = lambda: lgn.check(fn(*args, stream=s))
+        elif variant == "lse":
+            fn = lgn.lgn_linear_lse_f32 if w.dtype == "f32" else lgn.lgn_linear_lse_bf16
+            ws, nb_lse = self.ws, lgn.lgn_lse_workspace_bytes(w.M, w.N)
+            lse_args = (d["x"], d["W"], d["b_lin"], w.M, w.K, w.N, out, ws, nb_lse)
+            self.launch = lambda: lgn.check(fn(*lse_args, stream=s))
         else:
             fn = lgn.lgn_forward_twopass_f32 if w.dtype == "f32" else lgn.lgn_forward_twopass_bf16
             nb = lgn.lgn_twopass_workspace_bytes(w.M, w.N)
@@ -141,8 +151,11 @@ class Runner:
         idx = torch.from_numpy(rows).to(self.out.device)
         y = self.out[idx].cpu().numpy().astype(np.float64)
         i = self.inp
-        ref = oracle.lgn_forward(i["x"][rows], i["W"], i["b_lin"], i["b_add"], i["gamma"],
-                                 i["beta"], self.w.G, self.w.eps)
+        if self.variant == "lse":
+            ref = oracle.linear_lse_forward(i["x"][rows], i["W"], i["b_lin"])
+        else:
+            ref = oracle.lgn_forward(i["x"][rows], i["W"], i["b_lin"], i["b_add"], i["gamma"],
+                                     i["beta"], self.w.G, self.w.eps)
         return float(np.max(np.abs(y - ref))), len(rows)
 
 
@@ -211,7 +224,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--variant", default="fused", choices=["fused", "twopass"])
+    ap.add_argument("--variant", default="fused", choices=["fused", "twopass", "lse"],
+                    help="lse: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 (use with an "
+                         "m1024_k8192_n8192_lse_* workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (bf16, wide group, two-pass)")
@@ -285,7 +300,8 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic_for(w.name, args.variant),
             "kernel_ms_mean": round(kmean, 4),
-            "kernel": "lgn_fused_kernel" if args.variant == "fused" else "gemm+epilogue",
+            "kernel": {"fused": "lgn_fused_kernel", "twopass": "gemm+epilogue",
+                       "lse": "lse partial+finish"}[args.variant],
         },
         "check": {"rows": nrows, "max_abs_err_vs_oracle": err},
     }
@@ -297,19 +313,22 @@ def main():
         extra = []
         for name, variant in (("m32768_k1024_n4096_g64_bf16", "fused"),
                               ("m16384_k2048_n8192_g8_f32", "fused"),
-                              (DEFAULT_WORKLOAD, "twopass")):
+                              (DEFAULT_WORKLOAD, "twopass"),
+                              ("m1024_k8192_n8192_lse_f32", "lse"),
+                              ("m1024_k8192_n8192_lse_bf16", "lse")):
             if name == w.name and variant == args.variant:
                 continue
             we = get_workload(name)
             re = Runner(we, variant)
-            wl, km_mean = re.time(50, 5, min_warm_ms=100.0)
+            n_extra = 50
+            wl, km_mean = re.time(n_extra, 5, min_warm_ms=100.0)
             ach = we.flops / (km_mean * 1e-3) / 1e12
             e2, _ = re.check_rows(4)
             eprint("[bench] %s/%s: kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f), err %.2e"
                    % (name, variant, km_mean, ach, 100 * ach / PEAK_TFLOPS[we.dtype],
                       PEAK_TFLOPS[we.dtype], e2))
             extra.append({"workload": name, "variant": variant, "dtype": we.dtype,
-                          "ms_per_step": round(wl / 20 * 1e3, 4), "kernel_ms_mean": round(km_mean, 4),
+                          "ms_per_step": round(wl / n_extra * 1e3, 4), "kernel_ms_mean": round(km_mean, 4),
                           "tflops": round(ach, 3), "frac_of_peak": round(ach / PEAK_TFLOPS[we.dtype], 4),
                           "max_abs_err_vs_oracle": e2})
             del re

@@ -19,18 +19,19 @@ static hipError_t launch_lse_partial_cfg(const typename dt_traits<DT>::storage *
                          dim3(Cfg::NT), stream, x, W, b, M, K, N, part, tiles_m, tiles_n);
 }
 
-// 128 x 256 tiles of 8 waves (64 x 64 each): at the transcript's shape
-// (1024 x 8192 outputs) that is 256 workgroups, one per CU, each running the
-// whole K.  LDS DMA ring when K is a multiple of its stage depth, else the
-// register-staged core.
+// 128 x 256 tiles of 4 waves (128 x 64 each): at the transcript's shape
+// (1024 x 8192 outputs) that is 256 workgroups, each running the whole K.
+// The 4-stage LDS DMA ring (96 KiB) also keeps the dispatcher from placing
+// two workgroups on one CU while another CU idles.  K not a multiple of the
+// stage depth takes the register-staged core.
 template <class DT>
 static hipError_t launch_lse(const typename dt_traits<DT>::storage *x,
                              const typename dt_traits<DT>::storage *W, const float *b, int M,
                              int K, int N, float *out, void *workspace, hipStream_t stream) {
-    typedef TileCfg<DT, 128, kLseTileChannels, 2, 4, 64, 2> Cfg;
+    typedef TileCfg<DT, 128, kLseTileChannels, 1, 4, 64, 2> Cfg;
     float2 *part = reinterpret_cast<float2 *>(workspace);
     const hipError_t e =
-        K % Cfg::BK == 0 ? launch_lse_partial_cfg<DT, Cfg, 3>(x, W, b, M, K, N, part, stream)
+        K % Cfg::BK == 0 ? launch_lse_partial_cfg<DT, Cfg, 4>(x, W, b, M, K, N, part, stream)
                          : launch_lse_partial_cfg<DT, Cfg, 0>(x, W, b, M, K, N, part, stream);
     if (e != hipSuccess) return e;
     const int tiles_n = (N + kLseTileChannels - 1) / kLseTileChannels;
