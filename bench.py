@@ -23,7 +23,6 @@ cpu_baseline: the fp64 CPU oracle timed on the host on the first S rows of the
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -42,9 +41,20 @@ def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha() -> str:
+# Sources each variant's kernels are built from (a change to any of them
+# voids that variant's stored counter values).
+KERNEL_SOURCES = {
+    "fused": ("lgn_device.hpp", "lgn_fused.hpp", "lgn_fused_impl.hpp", "lgn_fused_f32.hip",
+              "lgn_fused_bf16.hip"),
+    "twopass": ("lgn_device.hpp", "lgn_twopass.hpp", "lgn_twopass.hip"),
+    "lse": ("lgn_device.hpp", "lgn_lse.hpp", "lgn_lse.hip"),
+}
+
+
+def kernel_sources_sha(variant: str) -> str:
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "gemm_activation_groupnorm_amd", "csrc", "*")))
+    csrc = os.path.join(ROOT, "gemm_activation_groupnorm_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in KERNEL_SOURCES[variant]]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -59,7 +69,7 @@ def traffic_for(workload: str, variant: str):
     with open(path) as f:
         data = json.load(f)
     rec = data.get("%s/%s" % (workload, variant))
-    if not rec or rec.get("src_sha") != kernel_sources_sha():
+    if not rec or rec.get("src_sha") != kernel_sources_sha(variant):
         return None
     return rec.get("traffic_bytes")
 

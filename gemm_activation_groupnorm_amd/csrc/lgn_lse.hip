@@ -35,7 +35,7 @@ static hipError_t launch_lse(const typename dt_traits<DT>::storage *x,
                          : launch_lse_partial_cfg<DT, Cfg, 0>(x, W, b, M, K, N, part, stream);
     if (e != hipSuccess) return e;
     const int tiles_n = (N + kLseTileChannels - 1) / kLseTileChannels;
-    return launch_kernel(lgn_lse_finish_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256),
+    return launch_kernel(lgn_lse_finish_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256),
                          stream, part, M, tiles_n, out);
 }
 

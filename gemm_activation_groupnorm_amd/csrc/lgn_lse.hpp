@@ -8,8 +8,9 @@
 // sample row of the tile, its BC values z to a partial (max, sum exp(z - max))
 // -- in registers per lane, with lane^32, then across the waves of the tile
 // through LDS, always in a fixed order -- and writes that pair to
-// part[row][tile column].  Kernel 2 merges a row's partials in column order
-// and applies the scalar activations.  No M x N intermediate is written.
+// part[row][tile column].  Kernel 2 (one wave per row) merges a row's
+// partials in a fixed order and applies the scalar activations.  No M x N
+// intermediate is written.
 #pragma once
 
 #include "lgn_device.hpp"
@@ -137,20 +138,36 @@ __device__ __forceinline__ float gelu_erf(float v) {
     return v * (0.5f * (1.0f + erff(v * 0.70710678118654752f)));
 }
 
-// Kernel 2: one thread per row.
+// Kernel 2: one wave per row.  Lane t < tiles_n holds the row's partial of
+// channel tile t (lanes t, t+64, ... for more than 64 tiles, merged in tile
+// order); an xor butterfly then merges the lanes, each pair in lower-lane-
+// first order, so that both lanes of a pair hold the same bits and lane 0
+// ends with the merge of every tile in a fixed order.
 __global__ __launch_bounds__(256) void lgn_lse_finish_kernel(const float2 *__restrict__ part,
                                                              int M, int tiles_n,
                                                              float *__restrict__ out) {
-    const int row = blockIdx.x * 256 + threadIdx.x;
-    if (row >= M) return;
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;   // whole wave leaves together
     const float2 *p = part + (size_t)row * (size_t)tiles_n;
-    float m = p[0].x, s = p[0].y;
-    for (int t = 1; t < tiles_n; ++t) lse_merge(m, s, p[t].x, p[t].y);
-    // s >= 1: the row maximum contributes e^0
-    const float l = m + __builtin_amdgcn_logf(s) * 0.69314718055994531f;
-    float v = leaky_relu_001(leaky_relu_001(l));
-    v = gelu_erf(gelu_erf(v));
-    out[row] = v;
+    float m = -__builtin_inff(), s = 0.f;
+    for (int t = lane; t < tiles_n; t += 64) lse_merge(m, s, p[t].x, p[t].y);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float om = __shfl_xor(m, off);
+        const float os = __shfl_xor(s, off);
+        const bool lower = (lane & off) == 0;
+        float a_m = lower ? m : om, a_s = lower ? s : os;
+        lse_merge(a_m, a_s, lower ? om : m, lower ? os : s);
+        m = a_m;
+        s = a_s;
+    }
+    if (lane == 0) {
+        // s >= 1: the row maximum contributes e^0
+        const float l = m + __builtin_amdgcn_logf(s) * 0.69314718055994531f;
+        float v = leaky_relu_001(leaky_relu_001(l));
+        out[row] = gelu_erf(gelu_erf(v));
+    }
 }
 
 }  // namespace lgn
