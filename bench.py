@@ -244,6 +244,9 @@ def main():
     ap.add_argument("--torch-context", action="store_true",
                     help="also time, for context only, torch's linear (vendor GEMM) and the "
                          "unfused torch pipeline on the same workload")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the forward, run the MFMA-ceiling probe (sustained MFMA rate "
+                         "and shader clock for zero and random operands) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the forward, run 5 plain device copies of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -256,6 +259,14 @@ def main():
               "the rows and is not run here (--gpus %d, WORLD_SIZE %d)." % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
+
+    if args.mfma_ceiling:
+        # a child process of its own: this process has not touched the GPU
+        import subprocess
+        from gemm_activation_groupnorm_amd import build as hip_build
+        if not os.path.exists(hip_build.PROBE):
+            hip_build.build_probe()
+        sys.exit(subprocess.run([hip_build.PROBE]).returncode)
 
     import torch
     if args.copy_calibration:

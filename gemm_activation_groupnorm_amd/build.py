@@ -18,6 +18,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "lgn")
 LIB = os.path.join(PKG, "liblgn.so")
+# Stand-alone measurement probe (not part of the library): the sustained MFMA
+# rate and shader clock for zero and random operands.
+PROBE_SRC = os.path.join(PKG, "probes", "mfma_ceiling.hip")
+PROBE = os.path.join(PKG, "probes", "mfma_ceiling")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -70,7 +74,19 @@ def build(jobs: int = 8, extra=()) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    """Compile the MFMA-ceiling probe executable next to its source."""
+    tmp = PROBE + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), *[f for f in HIPCC_FLAGS if f != "-fPIC"], PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SRC, " ".join(cmd), r.stderr))
+    os.replace(tmp, PROBE)
+    return PROBE
 
 
 if __name__ == "__main__":

@@ -28,7 +28,7 @@ template <class DT>
 static hipError_t launch_lse(const typename dt_traits<DT>::storage *x,
                              const typename dt_traits<DT>::storage *W, const float *b, int M,
                              int K, int N, float *out, void *workspace, hipStream_t stream) {
-    typedef TileCfg<DT, 128, kLseTileChannels, 1, 4, 64, 2> Cfg;
+    typedef TileCfg<DT, 128, kLseTileChannels, 1, 4, 64, 1> Cfg;
     float2 *part = reinterpret_cast<float2 *>(workspace);
     const hipError_t e =
         K % Cfg::BK == 0 ? launch_lse_partial_cfg<DT, Cfg, 4>(x, W, b, M, K, N, part, stream)
