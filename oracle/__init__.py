@@ -22,9 +22,18 @@ one scalar per row:
     l = log(sum_n exp(z[n]))         (row maximum first, then the shifted sum)
     out = gelu(gelu(leaky(leaky(l))))    leaky slope 0.01, exact gelu v*Phi(v)
 
+Third method (POPCORNBENCH transcript "Kimi-K2.6 l2_p60", the tail after its
+3-D transposed convolution), y [Nb, C, D, H, W]:
+
+    s = sigmoid(y) * y
+    per sample n and group g of C/G contiguous channels, over those channels
+    and every spatial position: mean, population variance
+    out = hardswish((s - mean) / sqrt(var + eps) * gamma[c] + beta[c])
+    hardswish(v) = v * clamp(v + 3, 0, 6) / 6
+
 All arithmetic is IEEE double in plain C (``lgn_oracle.c``), sequential sums,
 no FMA contraction.  Pins: ``tests/test_oracle_pins.py`` and
-``tests/test_lse_oracle_pins.py``.
+``tests/test_lse_oracle_pins.py``, ``tests/test_sgh_oracle_pins.py``.
 """
 from __future__ import annotations
 
@@ -88,6 +97,11 @@ def _load():
             lib.oracle_activation_array.restype = None
             lib.oracle_linear_lse_forward.argtypes = [dp, dp, dp, L, L, L, dp, dp]
             lib.oracle_linear_lse_forward.restype = ctypes.c_int
+            lib.oracle_hardswish.argtypes = [ctypes.c_double]
+            lib.oracle_hardswish.restype = ctypes.c_double
+            lib.oracle_swish_gn_hardswish.argtypes = [dp, dp, dp, L, L, L, L, ctypes.c_double,
+                                                      dp, dp, dp, dp]
+            lib.oracle_swish_gn_hardswish.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -200,6 +214,37 @@ def linear_lse_forward(x, W, b, return_lse: bool = False):
     if rc != 0:
         raise ValueError("oracle_linear_lse_forward failed with code %d" % rc)
     return (out, lse) if return_lse else out
+
+
+# ---- third method: Swish -> spatial GroupNorm -> HardSwish ----
+# (POPCORNBENCH transcript "Kimi-K2.6 l2_p60", problem statement)
+
+def hardswish(v) -> np.ndarray:
+    """HardSwish v * clamp(v + 3, 0, 6) / 6, elementwise."""
+    v = _f64(v)
+    f = _load().oracle_hardswish
+    return np.array([f(float(t)) for t in v.ravel()], dtype=np.float64).reshape(v.shape)
+
+
+def swish_gn_hardswish(y, gamma, beta, G: int, eps: float, return_parts: bool = False):
+    """y [Nb, C, *spatial] -> HardSwish(GroupNorm_G(Swish(y)) * gamma + beta), fp64.
+
+    With return_parts, also the normalised values before the affine and the
+    per-(sample, group) mean and population variance ([Nb, G])."""
+    y = _f64(y)
+    Nb, C = y.shape[0], y.shape[1]
+    S = int(np.prod(y.shape[2:])) if y.ndim > 2 else 1
+    ga, be = _f64(gamma), _f64(beta)
+    assert ga.shape == (C,) and be.shape == (C,)
+    out = np.empty_like(y)
+    norm = np.empty_like(y)
+    mean = np.empty((Nb, G), dtype=np.float64)
+    var = np.empty((Nb, G), dtype=np.float64)
+    rc = _load().oracle_swish_gn_hardswish(_ptr(y), _ptr(ga), _ptr(be), Nb, C, S, G, float(eps),
+                                           _ptr(out), _ptr(norm), _ptr(mean), _ptr(var))
+    if rc != 0:
+        raise ValueError("oracle_swish_gn_hardswish failed with code %d" % rc)
+    return (out, norm, mean, var) if return_parts else out
 
 
 def num_threads() -> int:

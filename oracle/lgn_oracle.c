@@ -7,6 +7,10 @@
  *
  *     out = GELU(GELU(LeakyReLU(LeakyReLU(logsumexp_n(x . W^T + b)))))
  *
+ * and for the third, the tail of a 3-D transposed convolution,
+ *
+ *     out = HardSwish(GroupNorm_G over channels x space (Swish(y)) * gamma + beta)
+ *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
  * header, table or helper with the HIP library and must never be called by
@@ -235,6 +239,65 @@ int oracle_linear_lse_forward(const double *x, const double *W, const double *b,
         free(row);
     }
     return failed ? -2 : 0;
+}
+
+/* ====================================================================== *
+ * Third method: the tail after a 3-D transposed convolution -- Swish, then
+ * GroupNorm over (channels of the group) x (all spatial positions), then
+ * HardSwish (POPCORNBENCH transcript "Kimi-K2.6 l2_p60", problem statement
+ * and its description of the group norm: mean and population variance over
+ * the group's channels and every spatial position of one sample, eps inside
+ * the square root, per-channel weight and bias; HardSwish x*clamp(x+3,0,6)/6).
+ * y is [Nb][C][S] with S = D*H*W flattened; out has the same layout.
+ * ====================================================================== */
+
+/* HardSwish: v * min(max(v + 3, 0), 6) / 6 */
+double oracle_hardswish(double v)
+{
+    double r = v + 3.0;
+    if (r < 0.0) r = 0.0;
+    if (r > 6.0) r = 6.0;
+    return v * r / 6.0;
+}
+
+/* Swish, then spatial GroupNorm (affine), then HardSwish, group by group.
+ * norm_out (optional) receives the normalised values before the affine,
+ * mean_out / var_out (optional, [Nb][G]) the group statistics.
+ * Returns 0, or -1 on bad arguments.                                        */
+int oracle_swish_gn_hardswish(const double *y, const double *gamma, const double *beta,
+                              long Nb, long C, long S, long G, double eps, double *out,
+                              double *norm_out, double *mean_out, double *var_out)
+{
+    if (Nb < 0 || C <= 0 || S <= 0 || G <= 0 || C % G != 0)
+        return -1;
+    long Cg = C / G;
+    long ng;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (ng = 0; ng < Nb * G; ++ng) {
+        long n = ng / G, g = ng % G;
+        size_t base = ((size_t)n * (size_t)C + (size_t)(g * Cg)) * (size_t)S;
+        size_t cnt = (size_t)Cg * (size_t)S;
+        double s = 0.0;
+        for (size_t i = 0; i < cnt; ++i)
+            s += oracle_swish(y[base + i]);
+        double mean = s / (double)cnt;
+        double ss = 0.0;
+        for (size_t i = 0; i < cnt; ++i) {
+            double d = oracle_swish(y[base + i]) - mean;
+            ss += d * d;
+        }
+        double var = ss / (double)cnt;
+        double denom = sqrt(var + eps);
+        for (size_t i = 0; i < cnt; ++i) {
+            long c = g * Cg + (long)(i / (size_t)S);
+            double nv = (oracle_swish(y[base + i]) - mean) / denom;
+            if (norm_out) norm_out[base + i] = nv;
+            out[base + i] = oracle_hardswish(nv * gamma[c] + beta[c]);
+        }
+        if (mean_out) mean_out[ng] = mean;
+        if (var_out) var_out[ng] = var;
+    }
+    return 0;
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
