@@ -190,6 +190,32 @@ lgn_status lgn_linear_lse_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float
     return linear_lse<DT_BF16>(x, W, b, M, K, N, out, workspace, workspace_bytes, stream);
 }
 
+size_t lgn_sgh_workspace_bytes(int Nb, int C, long long S, int G) {
+    if (Nb <= 0 || C <= 0 || S <= 0 || G <= 0 || C % G != 0) return 0;
+    const long long L = (long long)(C / G) * S;
+    if (L > 0x7fffffffLL) return 0;
+    return (size_t)Nb * (size_t)G * (size_t)lgn::sgh_parts(L) * 2 * sizeof(float);
+}
+
+lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const float *beta,
+                                      int Nb, int C, long long S, int G, float eps, float *out,
+                                      void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    if (Nb < 0 || C < 1 || S < 1 || G < 1 || C % G != 0) return LGN_ERR_INVALID_ARG;
+    if (!(eps > 0.0f) || !isfinite(eps)) return LGN_ERR_INVALID_ARG;
+    if (Nb == 0) return LGN_OK;   // empty batch: nothing is read or written
+    if ((long long)(C / G) * S > 0x7fffffffLL) return LGN_ERR_UNSUPPORTED;
+    if (!y || !gamma || !beta || !out || !workspace) return LGN_ERR_INVALID_ARG;
+    if (workspace_bytes < lgn_sgh_workspace_bytes(Nb, C, S, G)) return LGN_ERR_INVALID_ARG;
+    if (!aligned(y, 4) || !aligned(out, 4) || !aligned(gamma, 4) || !aligned(beta, 4) ||
+        !aligned(workspace, 8))
+        return LGN_ERR_UNSUPPORTED;
+    lgn_status s = check_device();
+    if (s != LGN_OK) return s;
+    return from_hip(lgn::launch_swish_gn_hardswish_f32(y, gamma, beta, Nb, C, S, G, eps, out,
+                                                       workspace, stream));
+}
+
 const char *lgn_status_string(lgn_status s) {
     switch (s) {
         case LGN_OK: return "LGN_OK: success";

@@ -47,6 +47,13 @@ hipError_t launch_linear_lse_f32(const float *x, const float *W, const float *b,
 hipError_t launch_linear_lse_bf16(const uint16_t *x, const uint16_t *W, const float *b, int M,
                                   int K, int N, float *out, void *workspace, hipStream_t stream);
 
+// Swish -> spatial GroupNorm -> HardSwish.  The workspace holds one
+// (mean, M2) float pair per chunk of kSghChunk elements of every group.
+long long sgh_parts(long long group_elems);
+hipError_t launch_swish_gn_hardswish_f32(const float *y, const float *gamma, const float *beta,
+                                         int Nb, int C, long long S, int G, float eps, float *out,
+                                         void *workspace, hipStream_t stream);
+
 hipError_t launch_gemm_bias_f32(const float *x, const float *W, const float *b_lin, int M,
                                 int K, int N, float *z, hipStream_t stream);
 hipError_t launch_gemm_bias_bf16(const uint16_t *x, const uint16_t *W, const float *b_lin,

@@ -71,6 +71,45 @@ LSE_WORKLOADS = [
 ]
 
 
+@dataclasses.dataclass(frozen=True)
+class SghWorkload:
+    """Swish -> spatial GroupNorm -> HardSwish on y [Nb, C, D, H, W]."""
+    name: str
+    Nb: int
+    C: int
+    D: int
+    H: int
+    W: int
+    G: int
+    seed: int
+    eps: float = 1e-5
+
+    @property
+    def S(self) -> int:
+        return self.D * self.H * self.W
+
+    @property
+    def elements(self) -> int:
+        return self.Nb * self.C * self.S
+
+
+# The third method at its transcript's shape: the output of a 3-D transposed
+# convolution (batch 128, 16 channels, 31 x 63 x 63) in 4 groups.
+SGH_WORKLOADS = [
+    SghWorkload("n128_c16_d31_h63_w63_g4_sgh_f32", 128, 16, 31, 63, 63, 4, 7),
+]
+
+
+def make_sgh_inputs(Nb: int, C: int, S: int, seed: int) -> Dict[str, np.ndarray]:
+    """y [Nb, C, S] ~ N(0, 1), gamma ~ 1 + 0.1 N(0, 1), beta ~ 0.1 N(0, 1) [C];
+    drawn in that order in float64 from default_rng(seed), rounded to float32."""
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((Nb, C, S)).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    return dict(y=y, gamma=gamma, beta=beta)
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits.
 

@@ -36,6 +36,8 @@ EXPORTS = (
     "lgn_lse_workspace_bytes",
     "lgn_linear_lse_f32",
     "lgn_linear_lse_bf16",
+    "lgn_sgh_workspace_bytes",
+    "lgn_swish_gn_hardswish_f32",
     "lgn_status_string",
     "lgn_version",
     "lgn_last_hip_error_string",
@@ -80,6 +82,9 @@ def _load():
         ("lgn_lse_workspace_bytes", [i, i], sz),
         ("lgn_linear_lse_f32", lse, i),
         ("lgn_linear_lse_bf16", lse, i),
+        ("lgn_sgh_workspace_bytes", [i, i, ctypes.c_longlong, i], sz),
+        ("lgn_swish_gn_hardswish_f32",
+         [vp, vp, vp, i, i, ctypes.c_longlong, i, f, vp, vp, sz, vp], i),
         ("lgn_status_string", [i], ctypes.c_char_p),
         ("lgn_version", [], ctypes.c_char_p),
         ("lgn_last_hip_error_string", [], ctypes.c_char_p),
@@ -171,6 +176,18 @@ def lgn_linear_lse_bf16(x, W, b, M, K, N, out, workspace, workspace_bytes, strea
     return _lib.lgn_linear_lse_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b, "f32"), M, K, N,
                                     _ptr(out, "f32"), _ptr(workspace, None), workspace_bytes,
                                     _stream(stream))
+
+
+def lgn_sgh_workspace_bytes(Nb: int, C: int, S: int, G: int) -> int:
+    return _lib.lgn_sgh_workspace_bytes(Nb, C, S, G)
+
+
+def lgn_swish_gn_hardswish_f32(y, gamma, beta, Nb, C, S, G, eps, out, workspace,
+                               workspace_bytes, stream=None) -> int:
+    return _lib.lgn_swish_gn_hardswish_f32(_ptr(y, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
+                                           Nb, C, S, G, eps, _ptr(out, "f32"),
+                                           _ptr(workspace, None), workspace_bytes,
+                                           _stream(stream))
 
 
 def lgn_status_string(status: int) -> str:

@@ -1,7 +1,7 @@
 /*
  * lgn.h -- C ABI of liblgn.so: fused Linear -> Swish -> +bias -> GroupNorm
- * on AMD Instinct MI355X (gfx950), and Linear -> logsumexp -> LeakyReLU x2 ->
- * GELU x2 (declared at the end).
+ * on AMD Instinct MI355X (gfx950), plus Linear -> logsumexp -> LeakyReLU x2 ->
+ * GELU x2 and Swish -> spatial GroupNorm -> HardSwish (declared at the end).
  *
  * The operation (POPCORNBENCH transcript "Kimi-K2.6 l2_p37", problem
  * statement and the passages fixing the forward order):
@@ -140,6 +140,34 @@ lgn_status lgn_linear_lse_f32(const float *x, const float *W, const float *b,
 lgn_status lgn_linear_lse_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float *b,
                                int M, int K, int N, float *out,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Third method: Swish -> spatial GroupNorm -> HardSwish ----
+ * (POPCORNBENCH transcript "Kimi-K2.6 l2_p60", the tail after its 3-D
+ * transposed convolution: Swish, then GroupNorm whose statistics run over a
+ * group's channels AND every spatial position of one sample, then
+ * HardSwish v * clamp(v + 3, 0, 6) / 6.)
+ *
+ *   s[n,c,i]   = y[n,c,i] * sigmoid(y[n,c,i])         y is [Nb, C, S] fp32,
+ *                                                     S = D*H*W flattened
+ *   per sample n and group g of C/G contiguous channels, over those channels
+ *   and all S positions: mean, population variance var
+ *   out[n,c,i] = hardswish((s - mean) / sqrt(var + eps) * gamma[c] + beta[c])
+ *
+ * Layouts: y and out [Nb][C][S] dense (NCDHW); gamma, beta [C] fp32.  `out`
+ * may be `y` itself (in place) but must not overlap it otherwise.  Two
+ * kernels: per-chunk statistics into `workspace`, then the apply pass;
+ * `workspace` must hold lgn_sgh_workspace_bytes(Nb, C, S, G) bytes (8 per
+ * 16384-element chunk of every group), be 8-byte aligned and overlap nothing
+ * else.  Rules: Nb >= 0 (0 is a no-op), C >= 1, S >= 1, G >= 1, C % G == 0,
+ * eps > 0 and finite; a group of (C/G)*S elements must fit in 2^31 - 1, else
+ * LGN_ERR_UNSUPPORTED.  y, out, gamma, beta need 4-byte alignment.  Results
+ * are bitwise reproducible. */
+size_t lgn_sgh_workspace_bytes(int Nb, int C, long long S, int G);
+
+lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const float *beta,
+                                      int Nb, int C, long long S, int G, float eps,
+                                      float *out, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *lgn_status_string(lgn_status s);

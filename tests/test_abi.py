@@ -165,3 +165,49 @@ def test_lse_unsupported_shapes(fn, bad):
 @pytest.mark.parametrize("fn", LSE_FNS, ids=lambda f: f.__name__)
 def test_lse_empty_batch_is_a_no_op(fn):
     assert _call_lse(fn, M=0, x=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK
+
+
+# ---- Swish -> spatial GroupNorm -> HardSwish ----
+
+SGH_GOOD = dict(Nb=2, C=16, S=123039, G=4, eps=1e-5)
+
+
+def _call_sgh(**kw):
+    a = dict(y=A, gamma=A, beta=A, out=A, ws=A, ws_bytes=1 << 40, **SGH_GOOD)
+    a.update(kw)
+    return lgn.lgn_swish_gn_hardswish_f32(a["y"], a["gamma"], a["beta"], a["Nb"], a["C"], a["S"],
+                                          a["G"], a["eps"], a["out"], a["ws"], a["ws_bytes"],
+                                          stream=0)
+
+
+def test_sgh_workspace_bytes():
+    # one (mean, M2) float pair per 16384-element chunk of each group
+    parts = -(-4 * 123039 // 16384)
+    assert lgn.lgn_sgh_workspace_bytes(128, 16, 123039, 4) == 128 * 4 * parts * 8
+    assert lgn.lgn_sgh_workspace_bytes(1, 4, 1, 4) == 4 * 1 * 8
+    assert lgn.lgn_sgh_workspace_bytes(0, 4, 10, 2) == 0
+    assert lgn.lgn_sgh_workspace_bytes(2, 6, 10, 4) == 0          # C % G != 0
+    assert lgn.lgn_sgh_workspace_bytes(1, 2, 1 << 31, 1) == 0     # group past 2^31 - 1
+
+
+SGH_INVALID = [dict(Nb=-1), dict(C=0), dict(S=0), dict(G=0), dict(C=16, G=3), dict(eps=0.0),
+               dict(eps=math.nan), dict(y=None), dict(gamma=None), dict(beta=None),
+               dict(out=None), dict(ws=None), dict(ws_bytes=lgn.lgn_sgh_workspace_bytes(
+                   2, 16, 123039, 4) - 1)]
+SGH_UNSUPPORTED = [dict(y=A + 2), dict(out=A + 1), dict(gamma=A + 2), dict(ws=A + 4),
+                   dict(C=4, G=1, S=1 << 30)]
+
+
+@pytest.mark.parametrize("bad", SGH_INVALID, ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_sgh_invalid_arguments(bad):
+    assert _call_sgh(**bad) == lgn.LGN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", SGH_UNSUPPORTED,
+                         ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_sgh_unsupported(bad):
+    assert _call_sgh(**bad) == lgn.LGN_ERR_UNSUPPORTED
+
+
+def test_sgh_empty_batch_is_a_no_op():
+    assert _call_sgh(Nb=0, y=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK

@@ -1,0 +1,97 @@
+"""GPU parity of Swish -> spatial GroupNorm -> HardSwish (through the C ABI)
+against the fp64 oracle; max abs error <= 2e-4 (fp32 data)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_activation_groupnorm_amd import lgn
+from gemm_activation_groupnorm_amd.inputs import SGH_WORKLOADS, make_sgh_inputs, sample_rows
+from gpu_helpers import TOL, log
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sgh(d, Nb, C, S, G, eps, out=None, stream=None):
+    if out is None:
+        out = torch.empty((Nb, C, S), dtype=torch.float32, device="cuda")
+    nb = lgn.lgn_sgh_workspace_bytes(Nb, C, S, G)
+    ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device="cuda")
+    lgn.check(lgn.lgn_swish_gn_hardswish_f32(d["y"], d["gamma"], d["beta"], Nb, C, S, G, eps, out,
+                                             ws, nb, stream=stream))
+    return out
+
+
+def dev(inp):
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in inp.items()}
+
+
+def _err(y, ref):
+    assert np.all(np.isfinite(y)), "non-finite GPU output"
+    return float(np.max(np.abs(y.astype(np.float64) - ref))) if y.size else 0.0
+
+
+SHAPES = [
+    # Nb, C, S, G
+    (2, 16, 123039 // 37, 4),   # odd S: group slabs start off 16-byte boundaries
+    (1, 4, 1, 4),               # one element per group
+    (3, 8, 100, 2),             # S < one wave's stride
+    (2, 6, 5000, 3),            # several chunks per group, ragged last chunk
+    (1, 2, 16384 * 2, 1),       # exactly two full chunks
+    (4, 16, 777, 16),           # one channel per group (instance-norm shape)
+    (2, 12, 4099, 1),           # one group over all channels
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "Nb%d_C%d_S%d_G%d" % s)
+def test_sgh_shapes(shape):
+    Nb, C, S, G = shape
+    log("sgh case Nb=%d C=%d S=%d G=%d" % shape)
+    inp = make_sgh_inputs(Nb, C, S, 700 + Nb + C + S + G)
+    out = run_sgh(dev(inp), Nb, C, S, G, 1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.swish_gn_hardswish(inp["y"], inp["gamma"], inp["beta"], G, 1e-5)
+    err = _err(out.cpu().numpy(), ref)
+    log("  max abs err %.3e" % err)
+    assert err <= TOL["f32"]
+
+
+def test_sgh_in_place_and_deterministic():
+    Nb, C, S, G = 2, 8, 20000, 4
+    inp = make_sgh_inputs(Nb, C, S, 71)
+    d = dev(inp)
+    a = run_sgh(d, Nb, C, S, G, 1e-5)
+    b = run_sgh(d, Nb, C, S, G, 1e-5)
+    buf = d["y"].clone()
+    run_sgh(dict(d, y=buf), Nb, C, S, G, 1e-5, out=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "run-to-run difference"
+    assert torch.equal(a, buf), "in place differs"
+
+
+def test_sgh_constant_group_gives_hardswish_beta():
+    # zero variance: eps alone scales the (fp32-rounded) deviations by
+    # 1/sqrt(eps) ~ 316, so the bar is the parity tolerance, not exactness
+    Nb, C, S, G = 1, 4, 3000, 2
+    inp = make_sgh_inputs(Nb, C, S, 72)
+    inp["y"][0, 2:4] = np.float32(0.7)
+    out = run_sgh(dev(inp), Nb, C, S, G, 1e-5).cpu().numpy()
+    ref = oracle.hardswish(inp["beta"][2:4].astype(np.float64))
+    assert np.max(np.abs(out[0, 2:4] - ref[:, None])) <= TOL["f32"]
+    full = oracle.swish_gn_hardswish(inp["y"], inp["gamma"], inp["beta"], G, 1e-5)
+    assert _err(out, full) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("wi", range(len(SGH_WORKLOADS)))
+def test_sgh_full_size_sampled(wi):
+    w = SGH_WORKLOADS[wi]
+    log("sgh workload %s" % w.name)
+    inp = make_sgh_inputs(w.Nb, w.C, w.S, w.seed)
+    out = run_sgh(dev(inp), w.Nb, w.C, w.S, w.G, w.eps)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.Nb, 4, seed=w.seed)   # whole samples: their groups are complete
+    ref = oracle.swish_gn_hardswish(inp["y"][rows], inp["gamma"], inp["beta"], w.G, w.eps)
+    err = _err(out[torch.from_numpy(rows).cuda()].cpu().numpy(), ref)
+    log("  sampled-sample max abs err %.3e" % err)
+    assert err <= TOL["f32"]
+    assert bool(torch.isfinite(out).all())
