@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused Linear+Swish+bias+GroupNorm TFLOP/s at M32768 K1024 N4096; % MFMA peak"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "m32768_k1024_n4096_g64_f32"
 
 
@@ -48,6 +49,7 @@ KERNEL_SOURCES = {
               "lgn_fused_bf16.hip"),
     "twopass": ("lgn_device.hpp", "lgn_twopass.hpp", "lgn_twopass.hip"),
     "lse": ("lgn_device.hpp", "lgn_lse.hpp", "lgn_lse.hip"),
+    "sgh": ("lgn_device.hpp", "lgn_sgh.hpp", "lgn_sgh.hip"),
 }
 
 
@@ -74,7 +76,37 @@ def traffic_for(workload: str, variant: str):
     return rec.get("traffic_bytes")
 
 
-class Runner:
+class _Timed:
+    """time(): W warm-up launches, then K timed ones on self.stream."""
+
+    def time(self, steps: int, warmup: int, min_warm_ms: float = 0.0):
+        """Wall time of `steps` back-to-back launches and the mean launch
+        duration from one HIP event pair on the launch stream around them.
+        `warmup` untimed launches first; with min_warm_ms > 0 the warm-up goes
+        on until that much GPU time has passed (the clocks ramp up under load
+        over tens of milliseconds)."""
+        import torch
+        t_warm = time.perf_counter()
+        for _ in range(warmup):
+            self.launch()
+        torch.cuda.synchronize()
+        while (time.perf_counter() - t_warm) * 1e3 < min_warm_ms:
+            for _ in range(max(1, warmup)):
+                self.launch()
+            torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(self.stream)
+        for _ in range(steps):
+            self.launch()
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, start.elapsed_time(end) / steps
+
+
+class Runner(_Timed):
     """Inputs resident on the GPU plus a launch() closure for one forward."""
 
     def __init__(self, w, variant: str):
@@ -126,32 +158,6 @@ class Runner:
             ws = self.ws
             self.launch = lambda: lgn.check(fn(*args, ws, nb, stream=s))
 
-    def time(self, steps: int, warmup: int, min_warm_ms: float = 0.0):
-        """Wall time of `steps` back-to-back launches and the mean launch
-        duration from one HIP event pair on the launch stream around them.
-        `warmup` untimed launches first; with min_warm_ms > 0 the warm-up goes
-        on until that much GPU time has passed (the clocks ramp up under load
-        over tens of milliseconds)."""
-        import torch
-        t_warm = time.perf_counter()
-        for _ in range(warmup):
-            self.launch()
-        torch.cuda.synchronize()
-        while (time.perf_counter() - t_warm) * 1e3 < min_warm_ms:
-            for _ in range(max(1, warmup)):
-                self.launch()
-            torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        start.record(self.stream)
-        for _ in range(steps):
-            self.launch()
-        end.record(self.stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return wall, start.elapsed_time(end) / steps
-
     def check_rows(self, nrows: int = 8):
         import numpy as np
         import oracle
@@ -166,6 +172,48 @@ class Runner:
         else:
             ref = oracle.lgn_forward(i["x"][rows], i["W"], i["b_lin"], i["b_add"], i["gamma"],
                                      i["beta"], self.w.G, self.w.eps)
+        return float(np.max(np.abs(y - ref))), len(rows)
+
+
+class SghRunner(_Timed):
+    """Swish -> spatial GroupNorm -> HardSwish on y [Nb, C, D*H*W], resident."""
+
+    def __init__(self, w):
+        import numpy as np
+        import torch
+        from gemm_activation_groupnorm_amd import lgn
+        from gemm_activation_groupnorm_amd.inputs import make_sgh_inputs
+
+        self.w, self.variant = w, "sgh"
+        t0 = time.perf_counter()
+        self.inp = make_sgh_inputs(w.Nb, w.C, w.S, w.seed)
+        self.d = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda:0")
+                  for k, v in self.inp.items()}
+        self.out = torch.empty_like(self.d["y"])
+        nb = lgn.lgn_sgh_workspace_bytes(w.Nb, w.C, w.S, w.G)
+        self.ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device="cuda:0")
+        torch.cuda.synchronize()
+        eprint("[bench] %s/sgh inputs ready in %.1f s" % (w.name, time.perf_counter() - t0))
+        self.stream = torch.cuda.current_stream()
+        d, s = self.d, self.stream
+        args = (d["y"], d["gamma"], d["beta"], w.Nb, w.C, w.S, w.G, w.eps, self.out, self.ws, nb)
+        self.launch = lambda: lgn.check(lgn.lgn_swish_gn_hardswish_f32(*args, stream=s))
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """One read of y and one write of out (gamma, beta are 2*C floats)."""
+        return 2 * self.w.elements * 4 + 2 * self.w.C * 4
+
+    def check_rows(self, nrows: int = 2):
+        """Max abs error against the oracle on `nrows` whole samples."""
+        import numpy as np
+        import oracle
+        import torch
+        from gemm_activation_groupnorm_amd.inputs import sample_rows
+        rows = sample_rows(self.w.Nb, nrows, seed=99)
+        y = self.out[torch.from_numpy(rows).to(self.out.device)].cpu().numpy().astype(np.float64)
+        ref = oracle.swish_gn_hardswish(self.inp["y"][rows], self.inp["gamma"], self.inp["beta"],
+                                        self.w.G, self.w.eps)
         return float(np.max(np.abs(y - ref))), len(rows)
 
 
@@ -228,15 +276,46 @@ def cpu_baseline(w, inp, seconds: float):
     }
 
 
+def sgh_main(args):
+    """One JSON line for the HBM-bound Swish -> spatial GroupNorm -> HardSwish
+    kernels (two launches per step), as GB/s of algorithmic traffic."""
+    from gemm_activation_groupnorm_amd.inputs import SGH_WORKLOADS
+    w = [x for x in SGH_WORKLOADS if x.name == args.workload]
+    if not w:
+        raise SystemExit("--variant sgh needs one of: %s" % [x.name for x in SGH_WORKLOADS])
+    w = w[0]
+    r = SghRunner(w)
+    wall, kmean = r.time(args.steps, args.warmup)
+    gbps = r.algorithmic_bytes / (kmean * 1e-3) / 1e9
+    err, nrows = r.check_rows()
+    eprint("[bench] %s/sgh: %.3f ms/step, kernel mean %.3f ms -> %.0f GB/s algorithmic (%.1f%% of "
+           "%.0f); sampled-sample max err %.2e"
+           % (w.name, wall / args.steps * 1e3, kmean, gbps, 100 * gbps / HBM_PEAK_GBPS,
+              HBM_PEAK_GBPS, err))
+    print(json.dumps({
+        "metric": "Swish->spatial GroupNorm->HardSwish algorithmic HBM GB/s", "value": round(gbps, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "Nb": w.Nb, "C": w.C, "D": w.D, "H": w.H, "W": w.W,
+                   "G": w.G, "eps": w.eps, "seed": w.seed, "variant": "sgh"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for(w.name, "sgh"), "kernel_ms_mean": round(kmean, 4),
+                     "kernel": "sgh stats+apply"},
+        "check": {"samples": nrows, "max_abs_err_vs_oracle": err}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--variant", default="fused", choices=["fused", "twopass", "lse"],
+    ap.add_argument("--variant", default="fused", choices=["fused", "twopass", "lse", "sgh"],
                     help="lse: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 (use with an "
-                         "m1024_k8192_n8192_lse_* workload)")
+                         "m1024_k8192_n8192_lse_* workload); sgh: Swish -> spatial GroupNorm -> "
+                         "HardSwish (use with an *_sgh_* workload; reports GB/s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (bf16, wide group, two-pass)")
@@ -284,6 +363,9 @@ def main():
         hip_build.build()
     from gemm_activation_groupnorm_amd.inputs import get_workload
 
+    if args.variant == "sgh":
+        sgh_main(args)
+        return
     w = get_workload(args.workload)
     r = Runner(w, args.variant)
     wall, kmean = r.time(args.steps, args.warmup)
@@ -353,6 +435,25 @@ def main():
                           "tflops": round(ach, 3), "frac_of_peak": round(ach / PEAK_TFLOPS[we.dtype], 4),
                           "max_abs_err_vs_oracle": e2})
             del re
+            torch.cuda.empty_cache()
+        from gemm_activation_groupnorm_amd.inputs import SGH_WORKLOADS
+        for ws_ in SGH_WORKLOADS:
+            if args.variant == "sgh":
+                continue
+            rs = SghRunner(ws_)
+            n_extra = 30
+            wl, km_mean = rs.time(n_extra, 3, min_warm_ms=100.0)
+            gbps = rs.algorithmic_bytes / (km_mean * 1e-3) / 1e9
+            e2, _ = rs.check_rows(2)
+            eprint("[bench] %s/sgh: kernel mean %.3f ms -> %.0f GB/s algorithmic (%.1f%% of %.0f), "
+                   "err %.2e" % (ws_.name, km_mean, gbps, 100 * gbps / HBM_PEAK_GBPS, HBM_PEAK_GBPS,
+                                 e2))
+            extra.append({"workload": ws_.name, "variant": "sgh", "dtype": "f32",
+                          "ms_per_step": round(wl / n_extra * 1e3, 4),
+                          "kernel_ms_mean": round(km_mean, 4), "algorithmic_gbps": round(gbps, 1),
+                          "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                          "max_abs_err_vs_oracle": e2})
+            del rs
             torch.cuda.empty_cache()
         res["extra"] = extra
 

@@ -204,10 +204,10 @@ lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const 
     if (Nb < 0 || C < 1 || S < 1 || G < 1 || C % G != 0) return LGN_ERR_INVALID_ARG;
     if (!(eps > 0.0f) || !isfinite(eps)) return LGN_ERR_INVALID_ARG;
     if (Nb == 0) return LGN_OK;   // empty batch: nothing is read or written
-    if ((long long)(C / G) * S > 0x7fffffffLL) return LGN_ERR_UNSUPPORTED;
+    if ((long long)(C / G) * S > 0x7fffffffLL || C / G > 8192) return LGN_ERR_UNSUPPORTED;
     if (!y || !gamma || !beta || !out || !workspace) return LGN_ERR_INVALID_ARG;
     if (workspace_bytes < lgn_sgh_workspace_bytes(Nb, C, S, G)) return LGN_ERR_INVALID_ARG;
-    if (!aligned(y, 4) || !aligned(out, 4) || !aligned(gamma, 4) || !aligned(beta, 4) ||
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(gamma, 4) || !aligned(beta, 4) ||
         !aligned(workspace, 8))
         return LGN_ERR_UNSUPPORTED;
     lgn_status s = check_device();

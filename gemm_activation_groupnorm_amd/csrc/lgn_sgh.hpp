@@ -15,8 +15,10 @@
 //   apply: every workgroup merges its group's chunk partials in the same
 //          fixed order (so all of a group's workgroups agree bit for bit),
 //          then writes hardswish(fma(swish(y), rstd*gamma, beta - mean*rstd*gamma)).
-// Loads are dwords, lane-contiguous (a wave reads 256 consecutive bytes):
-// slabs start on arbitrary element boundaries when S is odd.
+// Accesses are 16 bytes per lane over the 16-byte-aligned body of each chunk
+// (slabs start on arbitrary element boundaries when S is odd, so up to 3
+// elements at each end are done one by one), and each thread issues all of
+// its loads before using any, so they are in flight together.
 #pragma once
 
 #include "lgn_device.hpp"
@@ -73,58 +75,118 @@ __device__ __forceinline__ void block_merge(float &mean, float &m2, float &n, fl
     for (int w = 1; w < kSghThreads / 64; ++w) chan_merge(mean, m2, n, red[3 * w], red[3 * w + 1], red[3 * w + 2]);
 }
 
-// Stats kernel: grid = groups * parts.  part[group * parts + p] = (mean, M2).
+// A chunk [start, end) of absolute element indices, split for 16-byte
+// accesses: a head of < 4 elements up to the first multiple of 4, a body of
+// whole float4s, and a tail of < 4 elements.  y and out are 16-byte aligned.
+struct SghSplit {
+    long long start, a0, a1, end;
+    __device__ __forceinline__ SghSplit(long long s, long long e) : start(s), end(e) {
+        a0 = (s + 3) & ~3LL;
+        a1 = e & ~3LL;
+        if (a0 >= a1) a0 = a1 = e;   // no whole float4 inside: all head
+    }
+    __device__ __forceinline__ int body4() const { return (int)((a1 - a0) >> 2); }
+    // edge element handled by thread t (head: t < 4, tail: 64 <= t < 68), or -1
+    __device__ __forceinline__ long long edge(int t) const {
+        if (t < 4) return start + t < a0 ? start + t : -1;
+        if (t >= 64 && t < 68) return a1 + (t - 64) < end ? a1 + (t - 64) : -1;
+        return -1;
+    }
+};
+
+constexpr int kSghVec = kSghPerThread / 4;   // float4s per thread per chunk
+
+// Stats kernel: grid = (groups of this round) * parts, starting at group
+// g_first.  part[group * parts + p] = (mean, M2).
 __global__ __launch_bounds__(kSghThreads) void lgn_sgh_stats_kernel(
-    const float *__restrict__ y, int C, long long S, int G, int parts, float2 *__restrict__ part) {
+    const float *__restrict__ y, int C, long long S, int G, int parts, long long g_first,
+    float2 *__restrict__ part) {
     __shared__ float red[3 * (kSghThreads / 64)];
     const int tid = threadIdx.x;
-    const long long gi = blockIdx.x / parts;   // n * G + g
+    const long long gi = g_first + blockIdx.x / parts;   // n * G + g
     const int p = blockIdx.x % parts;
     const long long n = gi / G, g = gi % G;
     const long long cg = C / G;
     const long long L = cg * S;
-    const size_t base = (size_t)(n * C + g * cg) * (size_t)S;
+    const long long base = (n * C + g * cg) * S;
     const long long c0 = (long long)p * kSghChunk;
-    const int cnt = (int)(L - c0 < kSghChunk ? L - c0 : kSghChunk);
-    const float *src = y + base + c0;
+    const long long cnt = L - c0 < kSghChunk ? L - c0 : kSghChunk;
+    const SghSplit sp(base + c0, base + c0 + cnt);
+    const int nb4 = sp.body4();
+    const f32x4 *body = reinterpret_cast<const f32x4 *>(y + sp.a0);
 
-    float v[kSghPerThread];
-    int mine = 0;
+    f32x4 v[kSghVec];
 #pragma unroll
-    for (int k = 0; k < kSghPerThread; ++k) {
-        const int e = tid + k * kSghThreads;
-        v[k] = e < cnt ? swish(src[e]) : 0.f;
-        mine += e < cnt ? 1 : 0;
+    for (int k = 0; k < kSghVec; ++k) {
+        const int f = tid + k * kSghThreads;
+        v[k] = f < nb4 ? body[f] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    float sum = 0.f;
+    const long long ei = sp.edge(tid);
+    const float ev = ei >= 0 ? swish(y[ei]) : 0.f;
+    float sum = ei >= 0 ? ev : 0.f;
+    int mine = ei >= 0 ? 1 : 0;
 #pragma unroll
-    for (int k = 0; k < kSghPerThread; ++k) sum += v[k];
+    for (int k = 0; k < kSghVec; ++k) {
+        const bool ok = tid + k * kSghThreads < nb4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[k][j] = ok ? swish(v[k][j]) : 0.f;
+            sum += v[k][j];
+        }
+        mine += ok ? 4 : 0;
+    }
     const float nf = (float)mine;
     float mean = mine ? sum / nf : 0.f;
-    float m2 = 0.f;
+    float m2 = ei >= 0 ? (ev - mean) * (ev - mean) : 0.f;
 #pragma unroll
-    for (int k = 0; k < kSghPerThread; ++k) {
-        const float d = v[k] - mean;
-        m2 += tid + k * kSghThreads < cnt ? d * d : 0.f;
+    for (int k = 0; k < kSghVec; ++k) {
+        const bool ok = tid + k * kSghThreads < nb4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float d = v[k][j] - mean;
+            m2 += ok ? d * d : 0.f;
+        }
     }
     float nn = nf;
     block_merge(mean, m2, nn, red);
-    if (tid == 0) part[blockIdx.x] = make_float2(mean, m2);
+    if (tid == 0) part[gi * parts + p] = make_float2(mean, m2);
 }
 
 // Apply kernel: same grid; out may be y itself (each element is read and
-// then written by the same thread).
+// then written by the same thread).  gamma/beta of the group's channels are
+// folded with the statistics into per-channel (a, b) in LDS.  A thread loads
+// its float4s first (all in flight at once), then walks them with an
+// incrementally advanced channel index, keeping the coefficients of the
+// current channel and the next one in registers (a float4 crosses at most one
+// channel boundary when S >= 4).
+template <int MAXCG>
 __global__ __launch_bounds__(kSghThreads) void lgn_sgh_apply_kernel(
     const float *y, const float *__restrict__ gamma, const float *__restrict__ beta, int C,
-    long long S, int G, int parts, float eps, const float2 *__restrict__ part, float *out) {
+    long long S, int G, int parts, long long g_first, float eps, const float2 *__restrict__ part,
+    float *out) {
     __shared__ float red[3 * (kSghThreads / 64)];
+    __shared__ float coef_a[MAXCG + 1], coef_b[MAXCG + 1];
     const int tid = threadIdx.x;
-    const long long gi = blockIdx.x / parts;
+    const long long gi = g_first + blockIdx.x / parts;
     const int p = blockIdx.x % parts;
     const long long n = gi / G, g = gi % G;
-    const long long cg = C / G;
-    const long long L = cg * S;
-    const size_t base = (size_t)(n * C + g * cg) * (size_t)S;
+    const int cg = C / G;
+    const long long L = (long long)cg * S;
+    const long long base = (n * C + g * cg) * S;
+    const long long c0 = (long long)p * kSghChunk;
+    const long long cnt = L - c0 < kSghChunk ? L - c0 : kSghChunk;
+    const SghSplit sp(base + c0, base + c0 + cnt);
+    const int nb4 = sp.body4();
+    const f32x4 *body = reinterpret_cast<const f32x4 *>(y + sp.a0);
+
+    f32x4 v[kSghVec];
+#pragma unroll
+    for (int k = 0; k < kSghVec; ++k) {
+        const int f = tid + k * kSghThreads;
+        v[k] = f < nb4 ? body[f] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const long long ei = sp.edge(tid);
+    const float ev = ei >= 0 ? y[ei] : 0.f;
 
     // the group's statistics from its chunk partials, in a fixed order
     float mean = 0.f, m2 = 0.f, cntf = 0.f;
@@ -135,26 +197,59 @@ __global__ __launch_bounds__(kSghThreads) void lgn_sgh_apply_kernel(
     }
     block_merge(mean, m2, cntf, red);
     const float rstd = __builtin_amdgcn_rsqf(m2 / (float)L + eps);
+    for (int c = tid; c <= cg; c += kSghThreads) {
+        const int cc = c < cg ? c : cg - 1;   // one spare entry: "next channel" past the end
+        const float a = rstd * gamma[g * cg + cc];
+        coef_a[c] = a;
+        coef_b[c] = beta[g * cg + cc] - mean * a;
+    }
+    __syncthreads();
 
-    const long long c0 = (long long)p * kSghChunk;
-    const int cnt = (int)(L - c0 < kSghChunk ? L - c0 : kSghChunk);
-    const float *src = y + base + c0;
-    float *dst = out + base + c0;
-    // channel of this thread's first element, then advanced incrementally
-    long long rel = c0 + tid;
-    long long ch = rel / S;
-    long long off = rel - ch * S;
-    for (int e = tid; e < cnt; e += kSghThreads) {
-        const int c = (int)(g * cg + ch);
-        const float a = rstd * gamma[c];
-        const float b = beta[c] - mean * a;
-        const float t = __builtin_fmaf(swish(src[e]), a, b);
+    auto act = [](float t) {
         const float r = fminf(fmaxf(t + 3.0f, 0.0f), 6.0f);
-        dst[e] = t * r * (1.0f / 6.0f);
-        off += kSghThreads;
-        while (off >= S) {
-            off -= S;
-            ++ch;
+        return t * r * (1.0f / 6.0f);
+    };
+    if (ei >= 0) {
+        const int c = (int)((ei - base) / S);
+        out[ei] = act(__builtin_fmaf(swish(ev), coef_a[c], coef_b[c]));
+    }
+    f32x4 *obody = reinterpret_cast<f32x4 *>(out + sp.a0);
+    long long r = sp.a0 - base + 4LL * tid;   // group-relative index of this thread's float4
+    long long ch = r / S;
+    long long off = r - ch * S;
+    int cc = ch < cg ? (int)ch : cg;
+    float a0 = coef_a[cc], b0 = coef_b[cc], a1 = coef_a[cc < cg ? cc + 1 : cg],
+          b1 = coef_b[cc < cg ? cc + 1 : cg];
+#pragma unroll
+    for (int k = 0; k < kSghVec; ++k) {
+        const int f = tid + k * kSghThreads;
+        f32x4 o;
+        if (S >= 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool nxt = off + j >= S;
+                o[j] = act(__builtin_fmaf(swish(v[k][j]), nxt ? a1 : a0, nxt ? b1 : b0));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                long long cj = ch + (off + j) / S;
+                const int ci = cj < cg ? (int)cj : cg;
+                o[j] = act(__builtin_fmaf(swish(v[k][j]), coef_a[ci], coef_b[ci]));
+            }
+        }
+        if (f < nb4) obody[f] = o;
+        off += 4 * kSghThreads;
+        if (off >= S) {
+            while (off >= S) {
+                off -= S;
+                ++ch;
+            }
+            cc = ch < cg ? (int)ch : cg;
+            a0 = coef_a[cc];
+            b0 = coef_b[cc];
+            a1 = coef_a[cc < cg ? cc + 1 : cg];
+            b1 = coef_b[cc < cg ? cc + 1 : cg];
         }
     }
 }

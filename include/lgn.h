@@ -159,9 +159,9 @@ lgn_status lgn_linear_lse_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float
  * `workspace` must hold lgn_sgh_workspace_bytes(Nb, C, S, G) bytes (8 per
  * 16384-element chunk of every group), be 8-byte aligned and overlap nothing
  * else.  Rules: Nb >= 0 (0 is a no-op), C >= 1, S >= 1, G >= 1, C % G == 0,
- * eps > 0 and finite; a group of (C/G)*S elements must fit in 2^31 - 1, else
- * LGN_ERR_UNSUPPORTED.  y, out, gamma, beta need 4-byte alignment.  Results
- * are bitwise reproducible. */
+ * eps > 0 and finite; a group of (C/G)*S elements must fit in 2^31 - 1 and
+ * C/G must not exceed 8192, else LGN_ERR_UNSUPPORTED.  y and out need 16-byte
+ * alignment, gamma and beta 4-byte.  Results are bitwise reproducible. */
 size_t lgn_sgh_workspace_bytes(int Nb, int C, long long S, int G);
 
 lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const float *beta,

@@ -194,8 +194,8 @@ SGH_INVALID = [dict(Nb=-1), dict(C=0), dict(S=0), dict(G=0), dict(C=16, G=3), di
                dict(eps=math.nan), dict(y=None), dict(gamma=None), dict(beta=None),
                dict(out=None), dict(ws=None), dict(ws_bytes=lgn.lgn_sgh_workspace_bytes(
                    2, 16, 123039, 4) - 1)]
-SGH_UNSUPPORTED = [dict(y=A + 2), dict(out=A + 1), dict(gamma=A + 2), dict(ws=A + 4),
-                   dict(C=4, G=1, S=1 << 30)]
+SGH_UNSUPPORTED = [dict(y=A + 4), dict(out=A + 8), dict(gamma=A + 2), dict(ws=A + 4),
+                   dict(C=4, G=1, S=1 << 30), dict(C=16384, G=1, S=4)]
 
 
 @pytest.mark.parametrize("bad", SGH_INVALID, ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
