@@ -48,6 +48,8 @@ KERNEL_SOURCES = {
     "fused": ("lgn_device.hpp", "lgn_fused.hpp", "lgn_fused_impl.hpp", "lgn_fused_f32.hip",
               "lgn_fused_bf16.hip"),
     "twopass": ("lgn_device.hpp", "lgn_twopass.hpp", "lgn_twopass.hip"),
+    "wide": ("lgn_device.hpp", "lgn_fused.hpp", "lgn_wide.hpp", "lgn_wide_impl.hpp",
+             "lgn_wide_f32.hip", "lgn_wide_bf16.hip"),
     "lse": ("lgn_device.hpp", "lgn_lse.hpp", "lgn_lse.hip"),
     "sgh": ("lgn_device.hpp", "lgn_sgh.hpp", "lgn_sgh.hip"),
 }
@@ -137,6 +139,9 @@ class Runner(_Timed):
             self.out = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
         if variant == "twopass":
             self.ws = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        if variant == "wide":
+            nb_wide = lgn.lgn_wide_workspace_bytes(w.M, w.N)
+            self.ws = torch.empty(max(1, nb_wide // 4), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         eprint("[bench] %s/%s inputs ready in %.1f s" % (w.name, variant, time.perf_counter() - t0))
         self.stream = torch.cuda.current_stream()
@@ -147,6 +152,10 @@ class Runner(_Timed):
         if variant == "fused":
             fn = lgn.lgn_forward_f32 if w.dtype == "f32" else lgn.lgn_forward_bf16
             self.launch = lambda: lgn.check(fn(*args, stream=s))
+        elif variant == "wide":
+            fn = lgn.lgn_forward_wide_f32 if w.dtype == "f32" else lgn.lgn_forward_wide_bf16
+            ws, nb_wide = self.ws, lgn.lgn_wide_workspace_bytes(w.M, w.N)
+            self.launch = lambda: lgn.check(fn(*args, ws, nb_wide, stream=s))
         elif variant == "lse":
             fn = lgn.lgn_linear_lse_f32 if w.dtype == "f32" else lgn.lgn_linear_lse_bf16
             ws, nb_lse = self.ws, lgn.lgn_lse_workspace_bytes(w.M, w.N)
@@ -312,7 +321,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--variant", default="fused", choices=["fused", "twopass", "lse", "sgh"],
+    ap.add_argument("--variant", default="fused",
+                    choices=["fused", "twopass", "wide", "lse", "sgh"],
                     help="lse: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 (use with an "
                          "m1024_k8192_n8192_lse_* workload); sgh: Swish -> spatial GroupNorm -> "
                          "HardSwish (use with an *_sgh_* workload; reports GB/s)")
@@ -404,7 +414,7 @@ def main():
             "traffic": traffic_for(w.name, args.variant),
             "kernel_ms_mean": round(kmean, 4),
             "kernel": {"fused": "lgn_fused_kernel", "twopass": "gemm+epilogue",
-                       "lse": "lse partial+finish"}[args.variant],
+                       "wide": "wide partial+norm", "lse": "lse partial+finish"}[args.variant],
         },
         "check": {"rows": nrows, "max_abs_err_vs_oracle": err},
     }
@@ -417,6 +427,8 @@ def main():
         for name, variant in (("m32768_k1024_n4096_g64_bf16", "fused"),
                               ("m16384_k2048_n8192_g8_f32", "fused"),
                               (DEFAULT_WORKLOAD, "twopass"),
+                              ("m16384_k2048_n8192_g8_f32", "wide"),
+                              ("m16384_k2048_n8192_g1_f32", "wide"),
                               ("m1024_k8192_n8192_lse_f32", "lse"),
                               ("m1024_k8192_n8192_lse_bf16", "lse")):
             if name == w.name and variant == args.variant:

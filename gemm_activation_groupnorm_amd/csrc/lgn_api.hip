@@ -106,6 +106,27 @@ lgn_status forward_twopass(const T *x, const T *W, const float *b_lin, const flo
 }
 
 template <int DT, class T>
+lgn_status forward_wide(const T *x, const T *W, const float *b_lin, const float *b_add,
+                        const float *gamma, const float *beta, int M, int K, int N, int G,
+                        float eps, float *out, void *workspace, size_t ws_bytes,
+                        hipStream_t stream) {
+    lgn_status s = validate(DT, x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out);
+    if (s != LGN_OK || M == 0) return s;
+    if ((N / G) % 256 != 0) return LGN_ERR_UNSUPPORTED;
+    if (!aligned(gamma, 16) || !aligned(beta, 16)) return LGN_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < lgn_wide_workspace_bytes(M, N)) return LGN_ERR_INVALID_ARG;
+    if (!aligned(workspace, 8)) return LGN_ERR_UNSUPPORTED;
+    s = check_device();
+    if (s != LGN_OK) return s;
+    if (DT == DT_F32)
+        return from_hip(lgn::launch_wide_f32((const float *)x, (const float *)W, b_lin, b_add,
+                                             gamma, beta, M, K, N, G, eps, out, workspace,
+                                             stream));
+    return from_hip(lgn::launch_wide_bf16((const uint16_t *)x, (const uint16_t *)W, b_lin, b_add,
+                                          gamma, beta, M, K, N, G, eps, out, workspace, stream));
+}
+
+template <int DT, class T>
 lgn_status linear_lse(const T *x, const T *W, const float *b, int M, int K, int N, float *out,
                       void *workspace, size_t ws_bytes, hipStream_t stream) {
     if (M < 0 || K < 0 || N < 1) return LGN_ERR_INVALID_ARG;
@@ -170,6 +191,27 @@ lgn_status lgn_forward_twopass_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const 
                                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return forward_twopass<DT_BF16>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
                                     workspace, workspace_bytes, stream);
+}
+
+size_t lgn_wide_workspace_bytes(int M, int N) {
+    if (M <= 0 || N <= 0) return 0;
+    return (size_t)M * (size_t)((N + 255) / 256) * 2 * sizeof(float);
+}
+
+lgn_status lgn_forward_wide_f32(const float *x, const float *W, const float *b_lin,
+                                const float *b_add, const float *gamma, const float *beta, int M,
+                                int K, int N, int G, float eps, float *out, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    return forward_wide<DT_F32>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+                                workspace_bytes, stream);
+}
+
+lgn_status lgn_forward_wide_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float *b_lin,
+                                 const float *b_add, const float *gamma, const float *beta, int M,
+                                 int K, int N, int G, float eps, float *out, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return forward_wide<DT_BF16>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+                                 workspace_bytes, stream);
 }
 
 size_t lgn_lse_workspace_bytes(int M, int N) {

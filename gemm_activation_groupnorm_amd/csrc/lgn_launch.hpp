@@ -39,6 +39,16 @@ hipError_t launch_fused_bf16(const uint16_t *x, const uint16_t *W, const float *
                              const float *b_add, const float *gamma, const float *beta, int M,
                              int K, int N, int G, float eps, float *out, hipStream_t stream);
 
+// Groups wider than one tile (C = N/G a multiple of 256): the workspace
+// holds one (mean, M2) float pair per row and per 256-channel tile.
+hipError_t launch_wide_f32(const float *x, const float *W, const float *b_lin, const float *b_add,
+                           const float *gamma, const float *beta, int M, int K, int N, int G,
+                           float eps, float *out, void *workspace, hipStream_t stream);
+hipError_t launch_wide_bf16(const uint16_t *x, const uint16_t *W, const float *b_lin,
+                            const float *b_add, const float *gamma, const float *beta, int M,
+                            int K, int N, int G, float eps, float *out, void *workspace,
+                            hipStream_t stream);
+
 // Linear -> logsumexp -> LeakyReLU x2 -> GELU x2.  The workspace holds one
 // (max, sum) float pair per row and per tile of this many channels.
 constexpr int kLseTileChannels = 256;

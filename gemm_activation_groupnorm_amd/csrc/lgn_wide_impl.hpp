@@ -1,0 +1,47 @@
+// lgn_wide_impl.hpp -- launcher of the wide-group forward, shared by the
+// fp32 and bf16 instantiation units.
+#pragma once
+
+#include "lgn_launch.hpp"
+#include "lgn_wide.hpp"
+
+#include <type_traits>
+
+namespace lgn {
+
+// Kernel 1 uses the fused kernel's 256 x 256 tile and core (same schedules as
+// its C <= 64 case); K not a multiple of the stage depth takes the
+// register-staged core on a 128 x 256 tile.
+template <class DT>
+hipError_t launch_wide(const typename dt_traits<DT>::storage *x,
+                       const typename dt_traits<DT>::storage *W, const float *b_lin,
+                       const float *b_add, const float *gamma, const float *beta, int M, int K,
+                       int N, int G, float eps, float *out, void *workspace,
+                       hipStream_t stream) {
+    typedef typename std::conditional<std::is_same<DT, bf16_t>::value,
+                                      TileCfg<DT, 256, 256, 2, 4, 64, 2, 2, 2>,
+                                      TileCfg<DT, 256, 256, 2, 4, 64, 2>>::type Fast;
+    constexpr int RING = std::is_same<DT, bf16_t>::value ? 4 : 3;
+    typedef TileCfg<DT, 128, 256, 2, 4, 64, 2> Slow;
+    float2 *part = reinterpret_cast<float2 *>(workspace);
+    const int tiles_n = N / kWideTile;
+    hipError_t e;
+    if (K % Fast::BK == 0) {
+        const int tiles_m = (M + Fast::BS - 1) / Fast::BS;
+        e = launch_kernel(lgn_wide_partial_kernel<DT, Fast, RING>,
+                          dim3((unsigned)((long long)tiles_m * tiles_n)), dim3(Fast::NT), stream,
+                          x, W, b_lin, b_add, M, K, N, out, part, tiles_m, tiles_n);
+    } else {
+        const int tiles_m = (M + Slow::BS - 1) / Slow::BS;
+        e = launch_kernel(lgn_wide_partial_kernel<DT, Slow, 0>,
+                          dim3((unsigned)((long long)tiles_m * tiles_n)), dim3(Slow::NT), stream,
+                          x, W, b_lin, b_add, M, K, N, out, part, tiles_m, tiles_n);
+    }
+    if (e != hipSuccess) return e;
+    const long long pairs = (long long)M * G;
+    return launch_kernel(lgn_wide_norm_kernel<kWideTile>, dim3((unsigned)((pairs + 3) / 4)),
+                         dim3(256), stream, (const float2 *)part, gamma, beta, pairs, G,
+                         (N / G) / kWideTile, tiles_n, eps, out);
+}
+
+}  // namespace lgn

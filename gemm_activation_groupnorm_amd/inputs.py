@@ -62,6 +62,12 @@ WORKLOADS = [
 ]
 
 
+# Groups wider than one workgroup tile: LayerNorm over all 8192 channels of
+# the wide-group shape (the forward's G = 1 case).
+WIDE_WORKLOADS = [
+    Workload("m16384_k2048_n8192_g1_f32", 16384, 2048, 8192, 1, "f32", 8, x_scale=2.0),
+]
+
 # The second method (Linear -> logsumexp -> LeakyReLU x2 -> GELU x2) at the
 # shape of its transcript: batch 1024, 8192 input and 8192 output features.
 # It uses x, W and b_lin (as the linear bias) of the same draw; G is unused.
@@ -159,7 +165,7 @@ def workload_inputs(w: Workload) -> Dict[str, np.ndarray]:
 def get_workload(name_or_index) -> Workload:
     if isinstance(name_or_index, int):
         return WORKLOADS[name_or_index]
-    for w in WORKLOADS + LSE_WORKLOADS:
+    for w in WORKLOADS + WIDE_WORKLOADS + LSE_WORKLOADS:
         if w.name == name_or_index:
             return w
     raise KeyError(name_or_index)

@@ -33,6 +33,9 @@ EXPORTS = (
     "lgn_twopass_workspace_bytes",
     "lgn_forward_twopass_f32",
     "lgn_forward_twopass_bf16",
+    "lgn_wide_workspace_bytes",
+    "lgn_forward_wide_f32",
+    "lgn_forward_wide_bf16",
     "lgn_lse_workspace_bytes",
     "lgn_linear_lse_f32",
     "lgn_linear_lse_bf16",
@@ -79,6 +82,9 @@ def _load():
         ("lgn_twopass_workspace_bytes", [i, i], sz),
         ("lgn_forward_twopass_f32", two, i),
         ("lgn_forward_twopass_bf16", two, i),
+        ("lgn_wide_workspace_bytes", [i, i], sz),
+        ("lgn_forward_wide_f32", two, i),
+        ("lgn_forward_wide_bf16", two, i),
         ("lgn_lse_workspace_bytes", [i, i], sz),
         ("lgn_linear_lse_f32", lse, i),
         ("lgn_linear_lse_bf16", lse, i),
@@ -160,6 +166,26 @@ def lgn_forward_twopass_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, o
                                          _ptr(beta, "f32"), M, K, N, G, eps, _ptr(out, "f32"),
                                          _ptr(workspace, None), workspace_bytes,
                                          _stream(stream))
+
+
+def lgn_wide_workspace_bytes(M: int, N: int) -> int:
+    return _lib.lgn_wide_workspace_bytes(M, N)
+
+
+def lgn_forward_wide_f32(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+                         workspace_bytes, stream=None) -> int:
+    return _lib.lgn_forward_wide_f32(_ptr(x, "f32"), _ptr(W, "f32"), _ptr(b_lin, "f32"),
+                                     _ptr(b_add, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
+                                     M, K, N, G, eps, _ptr(out, "f32"), _ptr(workspace, None),
+                                     workspace_bytes, _stream(stream))
+
+
+def lgn_forward_wide_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+                          workspace_bytes, stream=None) -> int:
+    return _lib.lgn_forward_wide_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b_lin, "f32"),
+                                      _ptr(b_add, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
+                                      M, K, N, G, eps, _ptr(out, "f32"), _ptr(workspace, None),
+                                      workspace_bytes, _stream(stream))
 
 
 def lgn_lse_workspace_bytes(M: int, N: int) -> int:

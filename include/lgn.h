@@ -169,6 +169,32 @@ lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const 
                                       float *out, void *workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
+/* Groups wider than one workgroup tile: the same forward as lgn_forward_f32
+ * for C = N/G a multiple of 256 (up to LayerNorm over all N when G = 1).  A
+ * group's statistics then cross workgroups: kernel 1 runs the fused GEMM
+ * tile, bias, Swish and bias, writes u = Swish(z) + b_add to `out` and, per
+ * row and 256-channel tile, the partial (mean, M2) into `workspace`; kernel
+ * 2 merges each (row, group)'s partials in tile order and normalises `out`
+ * in place.  `workspace` must hold lgn_wide_workspace_bytes(M, N) bytes (8
+ * per row per 256 channels), be 8-byte aligned and overlap nothing else.
+ * Rules as for lgn_forward_f32, plus (N/G) % 256 == 0 and 16-byte aligned
+ * gamma and beta, else LGN_ERR_UNSUPPORTED. */
+size_t lgn_wide_workspace_bytes(int M, int N);
+
+lgn_status lgn_forward_wide_f32(const float *x, const float *W,
+                                const float *b_lin, const float *b_add,
+                                const float *gamma, const float *beta,
+                                int M, int K, int N, int G, float eps,
+                                float *out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+lgn_status lgn_forward_wide_bf16(const lgn_bf16 *x, const lgn_bf16 *W,
+                                 const float *b_lin, const float *b_add,
+                                 const float *gamma, const float *beta,
+                                 int M, int K, int N, int G, float eps,
+                                 float *out, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *lgn_status_string(lgn_status s);
 

@@ -211,3 +211,43 @@ def test_sgh_unsupported(bad):
 
 def test_sgh_empty_batch_is_a_no_op():
     assert _call_sgh(Nb=0, y=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK
+
+
+# ---- groups wider than one tile ----
+
+WIDE_FNS = [lgn.lgn_forward_wide_f32, lgn.lgn_forward_wide_bf16]
+
+
+def _call_wide(fn, **kw):
+    a = dict(x=A, W=A, b_lin=A, b_add=A, gamma=A, beta=A, out=A, ws=A, ws_bytes=1 << 40,
+             M=64, K=32, N=1024, G=2, eps=1e-5)
+    a.update(kw)
+    return fn(a["x"], a["W"], a["b_lin"], a["b_add"], a["gamma"], a["beta"], a["M"], a["K"],
+              a["N"], a["G"], a["eps"], a["out"], a["ws"], a["ws_bytes"], stream=0)
+
+
+def test_wide_workspace_bytes():
+    assert lgn.lgn_wide_workspace_bytes(16384, 8192) == 16384 * 32 * 8
+    assert lgn.lgn_wide_workspace_bytes(3, 512) == 3 * 2 * 8
+    assert lgn.lgn_wide_workspace_bytes(0, 512) == 0
+
+
+@pytest.mark.parametrize("fn", WIDE_FNS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("bad", [dict(M=-1), dict(N=1024, G=3), dict(eps=0.0), dict(ws=None),
+                                 dict(ws_bytes=64 * 4 * 8 - 1), dict(gamma=None), dict(x=None)],
+                         ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_wide_invalid_arguments(fn, bad):
+    assert _call_wide(fn, **bad) == lgn.LGN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", WIDE_FNS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("bad", [dict(N=1024, G=8), dict(N=768, G=2), dict(gamma=A + 4),
+                                 dict(beta=A + 8), dict(ws=A + 4), dict(K=6), dict(x=A + 4)],
+                         ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_wide_unsupported(fn, bad):
+    assert _call_wide(fn, **bad) == lgn.LGN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", WIDE_FNS, ids=lambda f: f.__name__)
+def test_wide_empty_batch_is_a_no_op(fn):
+    assert _call_wide(fn, M=0, x=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK
