@@ -195,7 +195,7 @@ lgn_status lgn_forward_twopass_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const 
 
 size_t lgn_wide_workspace_bytes(int M, int N) {
     if (M <= 0 || N <= 0) return 0;
-    return (size_t)M * (size_t)((N + 255) / 256) * 2 * sizeof(float);
+    return (size_t)M * (size_t)((N + 63) / 64) * 2 * sizeof(float);
 }
 
 lgn_status lgn_forward_wide_f32(const float *x, const float *W, const float *b_lin,

@@ -49,15 +49,23 @@ struct TileParams {
 // CG = channels per group (power of two, 8 .. 1024).  The tile's channel
 // span BC is a multiple of CG, so every group lies inside one workgroup.
 // RING selects the GEMM core (0: register-staged, any K; >= 2: LDS DMA ring).
-template <class DT, class Cfg, int CG, int RING>
+// WIDE (groups wider than the tile; CG is then the wave's channel span WC):
+// instead of normalising, the kernel writes u = Swish(z) + b_add to `out` and,
+// per row and WC-channel span, the (mean, M2) of those WC values to
+// wide_part[row * (N / WC) + span]; a second kernel merges a group's spans and
+// normalises.  The epilogue keeps the per-sample-tile order of the normal
+// path (statistics, then that sample tile's stores), which measured faster
+// than reducing whole tiles across waves before storing.
+template <class DT, class Cfg, int CG, int RING, bool WIDE = false>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC)))
 void lgn_fused_kernel(
     const typename dt_traits<DT>::storage *__restrict__ x,
     const typename dt_traits<DT>::storage *__restrict__ W, const float *__restrict__ b_lin,
     const float *__restrict__ b_add, const float *__restrict__ gamma,
     const float *__restrict__ beta, int M, int K, int N, float eps, float *__restrict__ out,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, float2 *__restrict__ wide_part) {
     static_assert(Cfg::BC % CG == 0, "groups must not straddle workgroup tiles");
+    static_assert(!WIDE || CG == Cfg::WC, "the wide mode reduces each wave's channel span");
     constexpr int TS = Cfg::TS, TC = Cfg::TC;
     // Values of one (sample, group) held by one lane, and segments per lane.
     constexpr int SPAN = CG < Cfg::WC ? CG : Cfg::WC;   // channels of a group inside one wave
@@ -140,15 +148,20 @@ void lgn_fused_kernel(
     constexpr bool STAGED = Cfg::WC >= 64 && Cfg::WC <= 256 &&
                             (Cfg::NT / 64) * (32 * Cfg::WC * 4) <= Sel::SMEM;
     auto normalise = [&](int ts, int tc, int q, const float *rstd, const float *nmr) {
-        const int ct = wc0 + 32 * tc + 8 * q + 4 * h;
-        const int s = (tc * 16 + 4 * q) / NLOC;
-        const f32x4 g = Par::get(par, 2, ct);
-        const f32x4 bt = Par::get(par, 3, ct);
         f32x4 y;
+        if constexpr (WIDE) {   // u itself: the second kernel normalises
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            y[j] = __builtin_fmaf(__builtin_fmaf(acc[ts][tc][4 * q + j], rstd[s], nmr[s]), g[j],
-                                  bt[j]);
+            for (int j = 0; j < 4; ++j) y[j] = acc[ts][tc][4 * q + j];
+        } else {
+            const int ct = wc0 + 32 * tc + 8 * q + 4 * h;
+            const int s = (tc * 16 + 4 * q) / NLOC;
+            const f32x4 g = Par::get(par, 2, ct);
+            const f32x4 bt = Par::get(par, 3, ct);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                y[j] = __builtin_fmaf(__builtin_fmaf(acc[ts][tc][4 * q + j], rstd[s], nmr[s]),
+                                      g[j], bt[j]);
+        }
         return y;
     };
     auto finish = [&](int ts, const float *rstd, const float *nmr) {
@@ -184,6 +197,12 @@ void lgn_fused_kernel(
                 local_stats(ts, s, mean, m2);
                 rstd[s] = __builtin_amdgcn_rsqf(m2 * (1.0f / CG) + eps);
                 nmr[s] = -mean * rstd[s];
+                if constexpr (WIDE) {
+                    const int row = m0 + ws0 + 32 * ts + lr;
+                    if (h == 0 && row < M)
+                        wide_part[(size_t)row * (size_t)(N / Cfg::WC) + (n0 + wc0) / Cfg::WC] =
+                            make_float2(mean, m2);
+                }
             }
             finish(ts, rstd, nmr);
         }
@@ -221,6 +240,7 @@ void lgn_fused_kernel(
             }
             rstd[ts] = __builtin_amdgcn_rsqf(q2 * (1.0f / CG) + eps);
             nmr[ts] = -mu * rstd[ts];
+
         }
         if constexpr (STAGED) __syncthreads();   // partials read before the block area is reused
 #pragma unroll

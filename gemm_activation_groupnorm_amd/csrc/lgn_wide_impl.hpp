@@ -9,9 +9,9 @@
 
 namespace lgn {
 
-// Kernel 1 uses the fused kernel's 256 x 256 tile and core (same schedules as
-// its C <= 64 case); K not a multiple of the stage depth takes the
-// register-staged core on a 128 x 256 tile.
+// Kernel 1 is the fused kernel's 256 x 256 tile (same core and schedules as
+// its C <= 64 case) in WIDE mode; K not a multiple of the stage depth takes
+// the register-staged core on a 128 x 256 tile (also 64-channel wave spans).
 template <class DT>
 hipError_t launch_wide(const typename dt_traits<DT>::storage *x,
                        const typename dt_traits<DT>::storage *W, const float *b_lin,
@@ -24,24 +24,26 @@ hipError_t launch_wide(const typename dt_traits<DT>::storage *x,
     constexpr int RING = std::is_same<DT, bf16_t>::value ? 4 : 3;
     typedef TileCfg<DT, 128, 256, 2, 4, 64, 2> Slow;
     float2 *part = reinterpret_cast<float2 *>(workspace);
-    const int tiles_n = N / kWideTile;
+    const int tiles_n = N / 256;
     hipError_t e;
     if (K % Fast::BK == 0) {
         const int tiles_m = (M + Fast::BS - 1) / Fast::BS;
-        e = launch_kernel(lgn_wide_partial_kernel<DT, Fast, RING>,
+        e = launch_kernel(lgn_fused_kernel<DT, Fast, kWideSpan, RING, true>,
                           dim3((unsigned)((long long)tiles_m * tiles_n)), dim3(Fast::NT), stream,
-                          x, W, b_lin, b_add, M, K, N, out, part, tiles_m, tiles_n);
+                          x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, tiles_m, tiles_n,
+                          part);
     } else {
         const int tiles_m = (M + Slow::BS - 1) / Slow::BS;
-        e = launch_kernel(lgn_wide_partial_kernel<DT, Slow, 0>,
+        e = launch_kernel(lgn_fused_kernel<DT, Slow, kWideSpan, 0, true>,
                           dim3((unsigned)((long long)tiles_m * tiles_n)), dim3(Slow::NT), stream,
-                          x, W, b_lin, b_add, M, K, N, out, part, tiles_m, tiles_n);
+                          x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, tiles_m, tiles_n,
+                          part);
     }
     if (e != hipSuccess) return e;
     const long long pairs = (long long)M * G;
-    return launch_kernel(lgn_wide_norm_kernel<kWideTile>, dim3((unsigned)((pairs + 3) / 4)),
+    return launch_kernel(lgn_wide_norm_kernel<kWideSpan>, dim3((unsigned)((pairs + 3) / 4)),
                          dim3(256), stream, (const float2 *)part, gamma, beta, pairs, G,
-                         (N / G) / kWideTile, tiles_n, eps, out);
+                         (N / G) / kWideSpan, N / kWideSpan, eps, out);
 }
 
 }  // namespace lgn

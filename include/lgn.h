@@ -173,10 +173,10 @@ lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const 
  * for C = N/G a multiple of 256 (up to LayerNorm over all N when G = 1).  A
  * group's statistics then cross workgroups: kernel 1 runs the fused GEMM
  * tile, bias, Swish and bias, writes u = Swish(z) + b_add to `out` and, per
- * row and 256-channel tile, the partial (mean, M2) into `workspace`; kernel
- * 2 merges each (row, group)'s partials in tile order and normalises `out`
+ * row and 64 channels, the partial (mean, M2) into `workspace`; kernel 2
+ * merges each (row, group)'s partials in a fixed order and normalises `out`
  * in place.  `workspace` must hold lgn_wide_workspace_bytes(M, N) bytes (8
- * per row per 256 channels), be 8-byte aligned and overlap nothing else.
+ * per row per 64 channels), be 8-byte aligned and overlap nothing else.
  * Rules as for lgn_forward_f32, plus (N/G) % 256 == 0 and 16-byte aligned
  * gamma and beta, else LGN_ERR_UNSUPPORTED. */
 size_t lgn_wide_workspace_bytes(int M, int N);

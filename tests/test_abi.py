@@ -227,14 +227,14 @@ def _call_wide(fn, **kw):
 
 
 def test_wide_workspace_bytes():
-    assert lgn.lgn_wide_workspace_bytes(16384, 8192) == 16384 * 32 * 8
-    assert lgn.lgn_wide_workspace_bytes(3, 512) == 3 * 2 * 8
+    assert lgn.lgn_wide_workspace_bytes(16384, 8192) == 16384 * 128 * 8
+    assert lgn.lgn_wide_workspace_bytes(3, 512) == 3 * 8 * 8
     assert lgn.lgn_wide_workspace_bytes(0, 512) == 0
 
 
 @pytest.mark.parametrize("fn", WIDE_FNS, ids=lambda f: f.__name__)
 @pytest.mark.parametrize("bad", [dict(M=-1), dict(N=1024, G=3), dict(eps=0.0), dict(ws=None),
-                                 dict(ws_bytes=64 * 4 * 8 - 1), dict(gamma=None), dict(x=None)],
+                                 dict(ws_bytes=64 * 16 * 8 - 1), dict(gamma=None), dict(x=None)],
                          ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
 def test_wide_invalid_arguments(fn, bad):
     assert _call_wide(fn, **bad) == lgn.LGN_ERR_INVALID_ARG
