@@ -56,9 +56,11 @@ KERNEL_SOURCES = {
 
 
 def kernel_sources_sha(variant: str) -> str:
+    # the build script counts too: it decides how the kernels are packaged
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemm_activation_groupnorm_amd", "csrc")
     files = [os.path.join(csrc, f) for f in KERNEL_SOURCES[variant]]
+    files.append(os.path.join(ROOT, "gemm_activation_groupnorm_amd", "build.py"))
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
