@@ -13,8 +13,10 @@ namespace lgn {
 // (LDS DMA ring) -- BS samples x BC channels, waves along samples x channels:
 //   CG <= 64  : 256 x 256, 2 x 4 waves of 128 x 64; bf16: ring of 4 with the
 //               mid-stage barrier schedule; fp32: ring of 3
-//   CG == 128 : 256 x 128, 4 x 1 waves of 64 x 128, ring of 3
-//   CG == 256 : 128 x 256, 2 x 2 waves of 64 x 128 (2 waves per group), ring of 3
+//   CG == 128 : fp32: 256 x 128, 4 x 1 waves of 64 x 128, ring of 3;
+//               bf16: the CG <= 64 tile, 2 waves per group
+//   CG == 256 : fp32: 128 x 256, 2 x 2 waves of 64 x 128 (2 waves per group), ring of 3;
+//               bf16: the CG <= 64 tile, 4 waves per group
 //   CG == 512 :  64 x 512, 1 x 4 waves of 64 x 128 (4 waves per group), ring of 3
 //   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128 (8 waves per group), ring of 2,
 //                simple schedule (fragments read right before their MFMAs)
@@ -65,8 +67,12 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
                                       TileCfg<DT, 256, 256, 2, 4, 64, 2, 2, 2>,
                                       TileCfg<DT, 256, 256, 2, 4, 64, 2>>::type F64;
     constexpr int R64 = std::is_same<DT, bf16_t>::value ? 4 : 3;
-    typedef TileCfg<DT, 256, 128, 4, 1, 64, 2> F128;
-    typedef TileCfg<DT, 128, 256, 2, 2, 64> F256;
+    // bf16 keeps the 256 x 256 tile up to CG = 256 (groups then span 2 or 4
+    // waves, merged through LDS); fp32 measured faster on the narrower tiles
+    constexpr bool BF = std::is_same<DT, bf16_t>::value;
+    typedef typename std::conditional<BF, F64, TileCfg<DT, 256, 128, 4, 1, 64, 2>>::type F128;
+    typedef typename std::conditional<BF, F64, TileCfg<DT, 128, 256, 2, 2, 64>>::type F256;
+    constexpr int R128 = BF ? 4 : 3;
     typedef TileCfg<DT, 64, 512, 1, 4, 64> F512;
     typedef TileCfg<DT, 64, 1024, 1, 8, 64, 1, 0> F1024;   // simple schedule
     const int cg = N / G;
@@ -79,8 +85,8 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
         LGN_CASE(16, F64, R64, S64)
         LGN_CASE(32, F64, R64, S64)
         LGN_CASE(64, F64, R64, S64)
-        LGN_CASE(128, F128, 3, S128)
-        LGN_CASE(256, F256, 3, S256)
+        LGN_CASE(128, F128, R128, S128)
+        LGN_CASE(256, F256, R128, S256)
         LGN_CASE(512, F512, 3, S512)
         LGN_CASE(1024, F1024, 2, S1024)
         default: return hipErrorInvalidValue;

@@ -62,6 +62,8 @@ SHAPES = [
     (33, 16, 256, 4),       # 64, a single fp32 stage (bf16 takes the other core)
     (1000, 64, 768, 12),    # 64, ring shorter than its depth
     (520, 192, 1152, 9),    # 128, ragged
+    (333, 96, 512, 4),      # 128, 2 groups per 256-channel tile (bf16: 2 waves per group)
+    (300, 320, 768, 3),     # 256, 10 bf16 stages (bf16: 4 waves per group), ragged M
 ]
 
 
