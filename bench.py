@@ -109,6 +109,40 @@ class _Timed:
         wall = time.perf_counter() - t0
         return wall, start.elapsed_time(end) / steps
 
+    def distribution(self, launches: int = 50, flush_bytes: int = 0):
+        """Per-launch durations (one HIP event pair around each launch on the
+        launch stream): median, p10 and p90 in ms.  With flush_bytes > 0 a
+        buffer of that size is overwritten between launches (outside the event
+        pair), so that x and W no longer sit in L2 or MALL when a launch starts."""
+        import numpy as np
+        import torch
+        buf = None
+        if flush_bytes:
+            buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device=self.out.device)
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(launches)]
+        with torch.cuda.stream(self.stream):
+            for e0, e1 in pairs:
+                if buf is not None:
+                    buf.fill_(1.0)
+                e0.record(self.stream)
+                self.launch()
+                e1.record(self.stream)
+        torch.cuda.synchronize()
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in pairs])
+        del buf
+        return {"median_ms": round(float(np.median(ms)), 4),
+                "p10_ms": round(float(np.percentile(ms, 10)), 4),
+                "p90_ms": round(float(np.percentile(ms, 90)), 4)}
+
+    def distributions(self, launches: int = 50):
+        """Back-to-back and flushed (1 GiB overwritten between launches) per-launch timings."""
+        hot = self.distribution(launches)
+        cold = self.distribution(launches, flush_bytes=1 << 30)
+        return {"launches": launches, **hot, "flushed_median_ms": cold["median_ms"],
+                "flushed_p10_ms": cold["p10_ms"], "flushed_p90_ms": cold["p90_ms"],
+                "flush_bytes": 1 << 30}
+
 
 class Runner(_Timed):
     """Inputs resident on the GPU plus a launch() closure for one forward."""
@@ -331,6 +365,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (bf16, wide group, two-pass)")
+    ap.add_argument("--no-per-launch", action="store_true",
+                    help="skip the per-launch (median/p10/p90, flushed) timings, e.g. under a "
+                         "profiler whose kernel averages should cover the timed launches only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--torch-context", action="store_true",
                     help="also time, for context only, torch's linear (vendor GEMM) and the "
@@ -386,7 +423,12 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kmean * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    dist = None if args.no_per_launch else r.distributions()
     err, nrows = r.check_rows()
+    if dist:
+        eprint("[bench] %s/%s per launch: median %.3f ms (p10 %.3f, p90 %.3f); flushed median "
+               "%.3f ms" % (w.name, args.variant, dist["median_ms"], dist["p10_ms"], dist["p90_ms"],
+                            dist["flushed_median_ms"]))
     eprint("[bench] %s/%s: %.3f ms/step, kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f); "
            "sampled-row max err %.2e"
            % (w.name, args.variant, ms_per_step, kmean, achieved, 100 * achieved / peak, peak, err))
@@ -418,6 +460,7 @@ def main():
             "kernel": {"fused": "lgn_fused_kernel", "twopass": "gemm+epilogue",
                        "wide": "wide partial+norm", "lse": "lse partial+finish"}[args.variant],
         },
+        "per_launch": dist,
         "check": {"rows": nrows, "max_abs_err_vs_oracle": err},
     }
     inp = r.inp
@@ -429,6 +472,8 @@ def main():
         for name, variant in (("m32768_k1024_n4096_g64_bf16", "fused"),
                               ("m16384_k2048_n8192_g8_f32", "fused"),
                               (DEFAULT_WORKLOAD, "twopass"),
+                              ("m32768_k1024_n4096_g64_bf16", "twopass"),
+                              ("m16384_k2048_n8192_g8_f32", "twopass"),
                               ("m16384_k2048_n8192_g8_f32", "wide"),
                               ("m16384_k2048_n8192_g1_f32", "wide"),
                               ("m1024_k8192_n8192_lse_f32", "lse"),
@@ -440,6 +485,7 @@ def main():
             n_extra = 50
             wl, km_mean = re.time(n_extra, 5, min_warm_ms=100.0)
             ach = we.flops / (km_mean * 1e-3) / 1e12
+            dist_e = re.distributions() if (variant == "fused" and we.dtype == "bf16") else None
             e2, _ = re.check_rows(4)
             eprint("[bench] %s/%s: kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f), err %.2e"
                    % (name, variant, km_mean, ach, 100 * ach / PEAK_TFLOPS[we.dtype],
@@ -448,6 +494,8 @@ def main():
                           "ms_per_step": round(wl / n_extra * 1e3, 4), "kernel_ms_mean": round(km_mean, 4),
                           "tflops": round(ach, 3), "frac_of_peak": round(ach / PEAK_TFLOPS[we.dtype], 4),
                           "max_abs_err_vs_oracle": e2})
+            if dist_e:
+                extra[-1]["per_launch"] = dist_e
             del re
             torch.cuda.empty_cache()
         from gemm_activation_groupnorm_amd.inputs import SGH_WORKLOADS
