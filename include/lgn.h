@@ -170,8 +170,11 @@ lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const 
                                       hipStream_t stream);
 
 /* Groups wider than one workgroup tile: the same forward as lgn_forward_f32
- * for C = N/G a multiple of 256 (up to LayerNorm over all N when G = 1).  A
- * group's statistics then cross workgroups: kernel 1 runs the fused GEMM
+ * (POPCORNBENCH transcript "Kimi-K2.6 l2_p37", problem statement and forward
+ * order) for C = N/G a multiple of 256, up to LayerNorm over all N when G = 1.
+ * The statistics then cross workgroups and take the two-stage form (per-block
+ * partials, then a light second pass) that the "Kimi-K2.6 l2_p64" transcript
+ * plans for its row reduction wider than one block: kernel 1 runs the fused GEMM
  * tile, bias, Swish and bias, writes u = Swish(z) + b_add to `out` and, per
  * row and 64 channels, the partial (mean, M2) into `workspace`; kernel 2
  * merges each (row, group)'s partials in a fixed order and normalises `out`
