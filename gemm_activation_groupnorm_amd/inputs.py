@@ -116,6 +116,47 @@ def make_sgh_inputs(Nb: int, C: int, S: int, seed: int) -> Dict[str, np.ndarray]
     return dict(y=y, gamma=gamma, beta=beta)
 
 
+@dataclasses.dataclass(frozen=True)
+class LnConvWorkload:
+    """LayerNorm over [C, L] -> GELU -> Conv1d (kernel 3, dilation d, padding d)
+    -> + input, on x [B, C, L]."""
+    name: str
+    B: int
+    C: int
+    L: int
+    dilation: int
+    seed: int
+    eps: float = 1e-5
+    gelu_tanh: bool = False
+
+    @property
+    def flops(self) -> int:
+        """Convolution flops, 2 * B * L * C_out * (C_in * 3)."""
+        return 2 * self.B * self.L * self.C * self.C * 3
+
+
+# The fourth method at its transcript's shape: batch 32, 256 channels, 4096
+# positions, dilation 4; the GELU of nn.GELU() (exact).
+LNCONV_WORKLOADS = [
+    LnConvWorkload("b32_c256_l4096_d4_lnconv_f32", 32, 256, 4096, 4, 9),
+]
+
+
+def make_lnconv_inputs(B: int, C: int, L: int, seed: int) -> Dict[str, np.ndarray]:
+    """x [B, C, L] ~ N(0, 1); ln_w ~ 1 + 0.1 N(0, 1), ln_b ~ 0.1 N(0, 1) [C, L];
+    conv_w [C, C, 3] and conv_b [C] ~ U(-1/sqrt(3C), 1/sqrt(3C)) (nn.Conv1d's
+    default bound); drawn in that order in float64 from default_rng(seed),
+    rounded to float32."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, C, L)).astype(np.float32)
+    ln_w = (1.0 + 0.1 * rng.standard_normal((C, L))).astype(np.float32)
+    ln_b = (0.1 * rng.standard_normal((C, L))).astype(np.float32)
+    bound = 1.0 / np.sqrt(3.0 * C)
+    conv_w = rng.uniform(-bound, bound, (C, C, 3)).astype(np.float32)
+    conv_b = rng.uniform(-bound, bound, C).astype(np.float32)
+    return dict(x=x, ln_w=ln_w, ln_b=ln_b, conv_w=conv_w, conv_b=conv_b)
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits.
 

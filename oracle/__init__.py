@@ -31,9 +31,20 @@ Third method (POPCORNBENCH transcript "Kimi-K2.6 l2_p60", the tail after its
     out = hardswish((s - mean) / sqrt(var + eps) * gamma[c] + beta[c])
     hardswish(v) = v * clamp(v + 3, 0, 6) / 6
 
+Fourth method (POPCORNBENCH transcript "Kimi-K2.6 l2_p5", problem statement
+and its derivation of the convolution indices), x [B, C, L]:
+
+    per sample b, over all C*L values: mean, population variance
+    h = (x - mean) / sqrt(var + eps) * ln_w[c, p] + ln_b[c, p]     (affine [C, L])
+    g = GELU(h)                            (exact v*Phi(v), or the tanh form)
+    out[b, co, j] = conv_b[co] + x[b, co, j]
+                  + sum_ci sum_{t<3} conv_w[co, ci, t] * g[ci, j - d + t*d]
+    with g = 0 outside [0, L) (kernel 3, dilation d, zero padding d)
+
 All arithmetic is IEEE double in plain C (``lgn_oracle.c``), sequential sums,
 no FMA contraction.  Pins: ``tests/test_oracle_pins.py`` and
-``tests/test_lse_oracle_pins.py``, ``tests/test_sgh_oracle_pins.py``.
+``tests/test_lse_oracle_pins.py``, ``tests/test_sgh_oracle_pins.py``,
+``tests/test_lnconv_oracle_pins.py``.
 """
 from __future__ import annotations
 
@@ -102,6 +113,15 @@ def _load():
             lib.oracle_swish_gn_hardswish.argtypes = [dp, dp, dp, L, L, L, L, ctypes.c_double,
                                                       dp, dp, dp, dp]
             lib.oracle_swish_gn_hardswish.restype = ctypes.c_int
+            lib.oracle_gelu_tanh.argtypes = [ctypes.c_double]
+            lib.oracle_gelu_tanh.restype = ctypes.c_double
+            lp = ctypes.POINTER(ctypes.c_long)
+            lib.oracle_ln_gelu_conv1d.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, ctypes.c_double,
+                                                  ctypes.c_int, dp, dp, dp, dp]
+            lib.oracle_ln_gelu_conv1d.restype = ctypes.c_int
+            lib.oracle_ln_gelu_conv1d_cols.argtypes = [dp, dp, dp, dp, dp, L, L, L, L,
+                                                       ctypes.c_double, ctypes.c_int, lp, L, dp]
+            lib.oracle_ln_gelu_conv1d_cols.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -245,6 +265,58 @@ def swish_gn_hardswish(y, gamma, beta, G: int, eps: float, return_parts: bool = 
     if rc != 0:
         raise ValueError("oracle_swish_gn_hardswish failed with code %d" % rc)
     return (out, norm, mean, var) if return_parts else out
+
+
+# ---- fourth method: LayerNorm -> GELU -> dilated Conv1d -> + input ----
+# (POPCORNBENCH transcript "Kimi-K2.6 l2_p5", problem statement)
+
+def gelu_tanh(v) -> np.ndarray:
+    """GELU in its tanh form 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), elementwise."""
+    return _activation(v, 2)
+
+
+def _lnconv_args(x, ln_w, ln_b, conv_w, conv_b):
+    x = _f64(x)
+    B, C, L = x.shape
+    lw, lb, cw, cb = _f64(ln_w), _f64(ln_b), _f64(conv_w), _f64(conv_b)
+    assert lw.shape == (C, L) and lb.shape == (C, L)
+    assert cw.shape == (C, C, 3) and cb.shape == (C,)
+    return x, lw, lb, cw, cb, B, C, L
+
+
+def ln_gelu_conv1d(x, ln_w, ln_b, conv_w, conv_b, dilation: int, eps: float,
+                   gelu_tanh: bool = False, return_parts: bool = False):
+    """x [B, C, L] -> Conv1d_{k3, dilation d, padding d}(GELU(LayerNorm_{C,L}(x))) + x, fp64.
+
+    ln_w, ln_b [C, L] (the LayerNorm's elementwise affine); conv_w [C, C, 3]
+    (out, in, tap), conv_b [C].  With return_parts, also g = GELU(LayerNorm(x))
+    [B, C, L] and the per-sample mean and population variance [B]."""
+    x, lw, lb, cw, cb, B, C, L = _lnconv_args(x, ln_w, ln_b, conv_w, conv_b)
+    out = np.empty_like(x)
+    g = np.empty_like(x)
+    mean = np.empty(B, dtype=np.float64)
+    var = np.empty(B, dtype=np.float64)
+    rc = _load().oracle_ln_gelu_conv1d(_ptr(x), _ptr(lw), _ptr(lb), _ptr(cw), _ptr(cb), B, C, L,
+                                       int(dilation), float(eps), int(bool(gelu_tanh)), _ptr(out),
+                                       _ptr(g), _ptr(mean), _ptr(var))
+    if rc != 0:
+        raise ValueError("oracle_ln_gelu_conv1d failed with code %d" % rc)
+    return (out, g, mean, var) if return_parts else out
+
+
+def ln_gelu_conv1d_cols(x, ln_w, ln_b, conv_w, conv_b, dilation: int, eps: float, cols,
+                        gelu_tanh: bool = False) -> np.ndarray:
+    """Output columns out[b, :, j] of ln_gelu_conv1d for each (b, j) in cols: [len(cols), C]."""
+    x, lw, lb, cw, cb, B, C, L = _lnconv_args(x, ln_w, ln_b, conv_w, conv_b)
+    c = np.ascontiguousarray(np.asarray(cols, dtype=np.int64).reshape(-1, 2).astype(np.int_))
+    out = np.empty((c.shape[0], C), dtype=np.float64)
+    rc = _load().oracle_ln_gelu_conv1d_cols(
+        _ptr(x), _ptr(lw), _ptr(lb), _ptr(cw), _ptr(cb), B, C, L, int(dilation), float(eps),
+        int(bool(gelu_tanh)), c.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), c.shape[0],
+        _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_ln_gelu_conv1d_cols failed with code %d" % rc)
+    return out
 
 
 def num_threads() -> int:

@@ -11,6 +11,10 @@
  *
  *     out = HardSwish(GroupNorm_G over channels x space (Swish(y)) * gamma + beta)
  *
+ * and for the fourth, a pre-norm dilated convolution block on x [B, C, L],
+ *
+ *     out = Conv1d_{k=3, dilation d, zero padding d}(GELU(LayerNorm_{C,L}(x))) + x
+ *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
  * header, table or helper with the HIP library and must never be called by
@@ -201,11 +205,20 @@ void oracle_logsumexp_rows(const double *z, long M, long N, double *out)
         out[m] = oracle_logsumexp(z + (size_t)m * (size_t)N, N);
 }
 
-/* out[i] = f(in[i]); which = 0 LeakyReLU, 1 GELU */
+/* GELU in its tanh form, 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+ * (POPCORNBENCH transcript "Kimi-K2.6 l2_p5", the GELU its kernel evaluates). */
+double oracle_gelu_tanh(double v)
+{
+    const double k = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * v * (1.0 + tanh(k * (v + 0.044715 * v * v * v)));
+}
+
+/* out[i] = f(in[i]); which = 0 LeakyReLU, 1 GELU, 2 GELU (tanh form) */
 void oracle_activation_array(const double *in, double *out, long n, int which)
 {
     for (long i = 0; i < n; ++i)
-        out[i] = which == 0 ? oracle_leaky_relu(in[i]) : oracle_gelu(in[i]);
+        out[i] = which == 0 ? oracle_leaky_relu(in[i])
+                            : (which == 1 ? oracle_gelu(in[i]) : oracle_gelu_tanh(in[i]));
 }
 
 /* The whole second forward, row by row:
@@ -298,6 +311,157 @@ int oracle_swish_gn_hardswish(const double *y, const double *gamma, const double
         if (var_out) var_out[ng] = var;
     }
     return 0;
+}
+
+/* ---- Fourth method (POPCORNBENCH transcript "Kimi-K2.6 l2_p5", problem
+ * statement and its derivation of the convolution's indices):
+ *   x [B][C][L]; per sample b, LayerNorm over all C*L values of x[b]
+ *   (population variance, eps inside the square root) with an elementwise
+ *   affine ln_w, ln_b of shape [C][L]:
+ *       h[c][p] = (x[b][c][p] - mean_b) / sqrt(var_b + eps) * ln_w[c][p] + ln_b[c][p]
+ *       g[c][p] = GELU(h[c][p])                    (exact, or the tanh form)
+ *   then Conv1d C -> C, kernel 3, dilation d, zero padding d on both sides
+ *   (so L_out = L), with bias, then the residual input:
+ *       out[b][co][j] = conv_b[co] + x[b][co][j]
+ *                     + sum_{ci} sum_{t=0..2} conv_w[co][ci][t] * g[ci][j - d + t*d]
+ *   where g is 0 at positions outside [0, L).                              */
+
+/* Mean and population variance of n values, exact two-pass. */
+static void ln_moments(const double *v, size_t n, double *mean, double *var)
+{
+    double s = 0.0;
+    for (size_t i = 0; i < n; ++i)
+        s += v[i];
+    double mu = s / (double)n;
+    double ss = 0.0;
+    for (size_t i = 0; i < n; ++i) {
+        double d = v[i] - mu;
+        ss += d * d;
+    }
+    *mean = mu;
+    *var = ss / (double)n;
+}
+
+/* g of sample xb at (c, p): 0 outside [0, L). */
+static double ln_gelu_at(const double *xb, const double *ln_w, const double *ln_b, long L,
+                         double mean, double denom, int gelu_tanh, long c, long p)
+{
+    if (p < 0 || p >= L)
+        return 0.0;
+    size_t i = (size_t)c * (size_t)L + (size_t)p;
+    double h = (xb[i] - mean) / denom * ln_w[i] + ln_b[i];
+    return gelu_tanh ? oracle_gelu_tanh(h) : oracle_gelu(h);
+}
+
+/* One output value out[b][co][j] from sample b's g (given as a function of
+ * (c, p) through gb, a [C][L] array of g values). */
+static double conv_out_at(const double *gb, const double *xb, const double *conv_w,
+                          const double *conv_b, long C, long L, long d, long co, long j)
+{
+    double acc = 0.0;
+    for (long ci = 0; ci < C; ++ci)
+        for (long t = 0; t < 3; ++t) {
+            long p = j - d + t * d;
+            if (p < 0 || p >= L)
+                continue;
+            acc += conv_w[((size_t)co * (size_t)C + (size_t)ci) * 3 + (size_t)t] *
+                   gb[(size_t)ci * (size_t)L + (size_t)p];
+        }
+    return conv_b[co] + acc + xb[(size_t)co * (size_t)L + (size_t)j];
+}
+
+/* The whole fourth forward.  g_out (optional, [B][C][L]) receives g,
+ * mean_out / var_out (optional, [B]) the per-sample statistics.
+ * Returns 0, -1 on bad arguments, -2 if a buffer could not be allocated.   */
+int oracle_ln_gelu_conv1d(const double *x, const double *ln_w, const double *ln_b,
+                          const double *conv_w, const double *conv_b, long B, long C, long L,
+                          long d, double eps, int gelu_tanh, double *out, double *g_out,
+                          double *mean_out, double *var_out)
+{
+    if (B < 0 || C <= 0 || L <= 0 || d < 1)
+        return -1;
+    size_t n = (size_t)C * (size_t)L;
+    int bad = 0;
+    long b;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (b = 0; b < B; ++b) {
+        const double *xb = x + (size_t)b * n;
+        double *gb = malloc(n * sizeof(double));
+        if (!gb) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        double mean, var;
+        ln_moments(xb, n, &mean, &var);
+        double denom = sqrt(var + eps);
+        for (long c = 0; c < C; ++c)
+            for (long p = 0; p < L; ++p)
+                gb[(size_t)c * (size_t)L + (size_t)p] =
+                    ln_gelu_at(xb, ln_w, ln_b, L, mean, denom, gelu_tanh, c, p);
+        for (long co = 0; co < C; ++co)
+            for (long j = 0; j < L; ++j)
+                out[(size_t)b * n + (size_t)co * (size_t)L + (size_t)j] =
+                    conv_out_at(gb, xb, conv_w, conv_b, C, L, d, co, j);
+        if (g_out)
+            for (size_t i = 0; i < n; ++i)
+                g_out[(size_t)b * n + i] = gb[i];
+        if (mean_out) mean_out[b] = mean;
+        if (var_out) var_out[b] = var;
+        free(gb);
+    }
+    return bad ? -2 : 0;
+}
+
+/* Selected output columns of the fourth forward: for i < ncols, sample
+ * cols[2i] and position cols[2i+1], out[i][co] = out[cols[2i]][co][cols[2i+1]]
+ * for every co.  The statistics of each sample are taken over all of it; g
+ * is evaluated only at the positions the column's taps reach.
+ * Returns 0, -1 on bad arguments, -2 if a buffer could not be allocated.   */
+int oracle_ln_gelu_conv1d_cols(const double *x, const double *ln_w, const double *ln_b,
+                               const double *conv_w, const double *conv_b, long B, long C,
+                               long L, long d, double eps, int gelu_tanh, const long *cols,
+                               long ncols, double *out)
+{
+    if (B < 0 || C <= 0 || L <= 0 || d < 1 || ncols < 0)
+        return -1;
+    for (long i = 0; i < ncols; ++i)
+        if (cols[2 * i] < 0 || cols[2 * i] >= B || cols[2 * i + 1] < 0 || cols[2 * i + 1] >= L)
+            return -1;
+    size_t n = (size_t)C * (size_t)L;
+    int bad = 0;
+    long i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < ncols; ++i) {
+        long b = cols[2 * i], j = cols[2 * i + 1];
+        const double *xb = x + (size_t)b * n;
+        double mean, var;
+        ln_moments(xb, n, &mean, &var);
+        double denom = sqrt(var + eps);
+        /* g at the three tap positions of column j, as a [C][L] view is not
+         * needed: keep g[ci][t] for the taps only */
+        double *gt = malloc((size_t)C * 3 * sizeof(double));
+        if (!gt) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        for (long ci = 0; ci < C; ++ci)
+            for (long t = 0; t < 3; ++t)
+                gt[(size_t)ci * 3 + (size_t)t] =
+                    ln_gelu_at(xb, ln_w, ln_b, L, mean, denom, gelu_tanh, ci, j - d + t * d);
+        for (long co = 0; co < C; ++co) {
+            double acc = 0.0;
+            for (long ci = 0; ci < C; ++ci)
+                for (long t = 0; t < 3; ++t)
+                    acc += conv_w[((size_t)co * (size_t)C + (size_t)ci) * 3 + (size_t)t] *
+                           gt[(size_t)ci * 3 + (size_t)t];
+            out[(size_t)i * (size_t)C + (size_t)co] =
+                conv_b[co] + acc + xb[(size_t)co * (size_t)L + (size_t)j];
+        }
+        free(gt);
+    }
+    return bad ? -2 : 0;
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
