@@ -239,6 +239,35 @@ size_t lgn_sgh_workspace_bytes(int Nb, int C, long long S, int G) {
     return (size_t)Nb * (size_t)G * (size_t)lgn::sgh_parts(L) * 2 * sizeof(float);
 }
 
+size_t lgn_lnconv_workspace_bytes(int B, int C, int L) {
+    if (B <= 0 || C <= 0 || L <= 0) return 0;
+    const long long parts = lgn::sgh_parts((long long)C * L);
+    return lgn::lnconv_wt_bytes(C) + (size_t)B * (size_t)parts * 2 * sizeof(float);
+}
+
+lgn_status lgn_ln_gelu_conv1d_f32(const float *x, const float *ln_w, const float *ln_b,
+                                  const float *conv_w, const float *conv_b, int B, int C, int L,
+                                  int dilation, float eps, int gelu_tanh, float *out,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || C < 1 || L < 1 || dilation < 1) return LGN_ERR_INVALID_ARG;
+    if (!(eps > 0.0f) || !isfinite(eps)) return LGN_ERR_INVALID_ARG;
+    if (B == 0) return LGN_OK;   // empty batch: nothing is read or written
+    if (!x || !ln_w || !ln_b || !conv_w || !conv_b || !out || !workspace)
+        return LGN_ERR_INVALID_ARG;
+    if (out == x) return LGN_ERR_INVALID_ARG;   // the convolution reads neighbours of x
+    if (C % 128 != 0 || L % 4 != 0 || dilation > 16) return LGN_ERR_UNSUPPORTED;
+    if ((long long)C * L > 0x7fffffffLL) return LGN_ERR_UNSUPPORTED;
+    if (workspace_bytes < lgn_lnconv_workspace_bytes(B, C, L)) return LGN_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(ln_w, 16) || !aligned(ln_b, 16) || !aligned(out, 16) ||
+        !aligned(workspace, 16) || !aligned(conv_w, 4) || !aligned(conv_b, 4))
+        return LGN_ERR_UNSUPPORTED;
+    lgn_status s = check_device();
+    if (s != LGN_OK) return s;
+    return from_hip(lgn::launch_ln_gelu_conv1d_f32(x, ln_w, ln_b, conv_w, conv_b, B, C, L,
+                                                   dilation, eps, gelu_tanh, out, workspace,
+                                                   stream));
+}
+
 lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const float *beta,
                                       int Nb, int C, long long S, int G, float eps, float *out,
                                       void *workspace, size_t workspace_bytes,

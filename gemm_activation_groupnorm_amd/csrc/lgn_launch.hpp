@@ -60,6 +60,15 @@ hipError_t launch_linear_lse_bf16(const uint16_t *x, const uint16_t *W, const fl
 // Swish -> spatial GroupNorm -> HardSwish.  The workspace holds one
 // (mean, M2) float pair per chunk of kSghChunk elements of every group.
 long long sgh_parts(long long group_elems);
+
+// LayerNorm -> GELU -> dilated Conv1d -> + input (C % 128 == 0, L % 4 == 0,
+// dilation 1..16).  The workspace holds the packed weights
+// (lnconv_wt_bytes(C)) followed by the per-sample statistics partials.
+size_t lnconv_wt_bytes(int C);
+hipError_t launch_ln_gelu_conv1d_f32(const float *x, const float *ln_w, const float *ln_b,
+                                     const float *conv_w, const float *conv_b, int B, int C,
+                                     int L, int dilation, float eps, int gelu_tanh, float *out,
+                                     void *workspace, hipStream_t stream);
 hipError_t launch_swish_gn_hardswish_f32(const float *y, const float *gamma, const float *beta,
                                          int Nb, int C, long long S, int G, float eps, float *out,
                                          void *workspace, hipStream_t stream);

@@ -1,0 +1,220 @@
+// lgn_lnconv.hpp -- the fourth method: a pre-norm dilated convolution block
+// (POPCORNBENCH transcript "Kimi-K2.6 l2_p5", problem statement and its
+// derivation of the convolution's indices) on x [B][C][L]:
+//
+//   per sample b, over all C*L values: mean, population variance
+//   h = (x - mean) / sqrt(var + eps) * ln_w[c][p] + ln_b[c][p]     ln_w, ln_b [C][L]
+//   g = GELU(h)                                (exact, or the tanh form)
+//   out[b][co][j] = conv_b[co] + x[b][co][j] + sum_ci sum_{t<3} W[co][ci][t] * g[ci][j - d + t*d]
+//   g = 0 outside [0, L)                       (kernel 3, dilation d, zero padding d)
+//
+// The normalisation sits before the contraction, so it cannot be an
+// epilogue: its statistics come from a first pass (the spatial GroupNorm's
+// stats kernel without the Swish, one group of C*L values per sample), and
+// LayerNorm + GELU are applied to the activation tiles while they are staged
+// into LDS for the convolution.
+//
+// The convolution is an implicit GEMM on fp32 MFMA (v_mfma_f32_32x32x2_f32):
+//   D[co][j] = sum_{k = (t, ci)} Wt[t][ci][co] * g[ci][j - d + t*d]
+// operand A = weights (M = output channels), operand B = activations (N =
+// positions), K = 3 taps x C input channels.  In the 32x32 accumulator a lane
+// then holds one position and 16 output channels, so each store instruction
+// writes 32 consecutive positions of one channel row.
+#pragma once
+
+#include "lgn_sgh.hpp"
+
+namespace lgn {
+
+constexpr int kLcCo = 128;        // output channels per workgroup
+constexpr int kLcPos = 128;       // positions per workgroup
+constexpr int kLcKc = 16;         // input channels per stage (K = 3 * 16 per stage)
+constexpr int kLcThreads = 256;   // 4 waves: 2 (channels) x 2 (positions) of 64 x 64
+constexpr int kLcMaxHalo = 16;    // largest dilation handled (halo rounded up to 4)
+constexpr int kLcGP = kLcPos + 2 * kLcMaxHalo;   // LDS pitch of an activation row
+constexpr int kLcWf4 = 3 * kLcKc * kLcCo / 4 / kLcThreads;                 // weight float4s per thread
+constexpr int kLcGf4 = (kLcKc * kLcGP / 4 + kLcThreads - 1) / kLcThreads;  // activation float4s, at most
+
+// W [co][ci][t] -> Wt [t][ci][co]: the weights as K-major rows of output
+// channels, so a stage's weight slab is read with 16-byte loads.
+__global__ __launch_bounds__(256) void lgn_conv_wpack_kernel(const float *__restrict__ w, int C,
+                                                             float *__restrict__ wt) {
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long n = 3LL * C * C;
+    if (e >= n) return;
+    const int co = (int)(e % C);
+    const long long r = e / C;
+    const int ci = (int)(r % C);
+    const int t = (int)(r / C);
+    wt[e] = w[((size_t)co * C + ci) * 3 + t];
+}
+
+template <bool TANH>
+__device__ __forceinline__ float lc_gelu(float v) {
+    if constexpr (TANH) {
+        const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
+        return 0.5f * v * (1.0f + tanhf(u));
+    } else {
+        return 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
+    }
+}
+
+// The convolution with LayerNorm + GELU applied while staging.  Grid: one
+// workgroup per (sample, 128-position tile, 128-channel tile), channel tiles
+// fastest; the hardware id is remapped so each XCD gets a contiguous run.
+// part[b * parts + p] = (mean, M2) of chunk p (kSghChunk values) of sample b.
+// H = the dilation rounded up to a multiple of 4 (<= kLcMaxHalo).
+// Requires C % 128 == 0, L % 4 == 0, 1 <= d <= H <= 16; out must not overlap x.
+template <bool TANH>
+__global__ __launch_bounds__(kLcThreads) void lgn_lnconv_kernel(
+    const float *__restrict__ x, const float *__restrict__ ln_w, const float *__restrict__ ln_b,
+    const float *__restrict__ wt, const float *__restrict__ conv_b,
+    const float2 *__restrict__ part, int C, int L, int d, int H, int parts, float eps,
+    int tiles_l, int tiles_c, float *__restrict__ out) {
+    // weight rows: odd rows have their 32-float halves swapped (column ^ 32),
+    // so the two lane halves of a read (rows 2k, 2k+1) hit disjoint banks
+    __shared__ __attribute__((aligned(16))) float ws[2][3 * kLcKc][kLcCo];
+    __shared__ __attribute__((aligned(16))) float gs[2][kLcKc][kLcGP];
+    __shared__ float red[3 * (kLcThreads / 64)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 31, h = lane >> 5;
+    const int wc = wave & 1, wp = wave >> 1;
+
+    const int nblocks = gridDim.x;
+    int t_id = blockIdx.x;
+    if ((nblocks & 7) == 0) t_id = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
+    const int ct = t_id % tiles_c;
+    const int rest = t_id / tiles_c;
+    const int lt = rest % tiles_l;
+    const int b = rest / tiles_l;
+    const int co0 = ct * kLcCo;
+    const int j0 = lt * kLcPos;
+
+    // ---- the sample's statistics from its chunk partials, in a fixed order ----
+    const long long n = (long long)C * L;
+    float mean = 0.f, m2 = 0.f, cnt = 0.f;
+    for (int t = tid; t < parts; t += kLcThreads) {
+        const long long ctn = n - (long long)t * kSghChunk;
+        const float2 q = part[(size_t)b * parts + t];
+        chan_merge(mean, m2, cnt, q.x, q.y, (float)(ctn < kSghChunk ? ctn : kSghChunk));
+    }
+    block_merge(mean, m2, cnt, red);
+    const float rstd = __builtin_amdgcn_rsqf(m2 / (float)n + eps);
+    const float nmr = -mean * rstd;
+
+    const float *xb = x + (size_t)b * C * L;
+    const int win4 = (kLcPos + 2 * H) / 4;        // float4s per staged activation row
+    const int gtot = kLcKc * win4;
+
+    f32x4 rw[kLcWf4];
+    f32x4 rx[kLcGf4], rg[kLcGf4], rb[kLcGf4];
+
+    // global -> registers for stage s (input channels s*16 .. s*16+15)
+    auto load_stage = [&](int s) {
+        const int c0 = s * kLcKc;
+#pragma unroll
+        for (int q = 0; q < kLcWf4; ++q) {
+            const int f = tid + q * kLcThreads;
+            const int row = f >> 5, col4 = f & 31;     // row = t * 16 + cl
+            const int t = row / kLcKc, cl = row % kLcKc;
+            rw[q] = *reinterpret_cast<const f32x4 *>(
+                wt + ((size_t)(t * C + c0 + cl) * C + co0 + 4 * col4));
+        }
+#pragma unroll
+        for (int q = 0; q < kLcGf4; ++q) {
+            const int f = tid + q * kLcThreads;
+            const int cl = f / win4, col4 = f - cl * win4;
+            const int p = j0 - H + 4 * col4;
+            if (f < gtot && p >= 0 && p < L) {
+                const size_t o = (size_t)(c0 + cl) * L + p;
+                rx[q] = *reinterpret_cast<const f32x4 *>(xb + o);
+                rg[q] = *reinterpret_cast<const f32x4 *>(ln_w + o);
+                rb[q] = *reinterpret_cast<const f32x4 *>(ln_b + o);
+            }
+        }
+    };
+    // registers -> LDS buffer `buf`, LayerNorm + GELU on the way; 0 outside [0, L)
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < kLcWf4; ++q) {
+            const int f = tid + q * kLcThreads;
+            const int row = f >> 5;
+            *reinterpret_cast<f32x4 *>(&ws[buf][row][(4 * (f & 31)) ^ (32 * (row & 1))]) = rw[q];
+        }
+#pragma unroll
+        for (int q = 0; q < kLcGf4; ++q) {
+            const int f = tid + q * kLcThreads;
+            const int cl = f / win4, col4 = f - cl * win4;
+            const int p = j0 - H + 4 * col4;
+            if (f < gtot) {
+                f32x4 g = {0.f, 0.f, 0.f, 0.f};
+                if (p >= 0 && p < L) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        g[e] = lc_gelu<TANH>(
+                            __builtin_fmaf(__builtin_fmaf(rx[q][e], rstd, nmr), rg[q][e], rb[q][e]));
+                }
+                *reinterpret_cast<f32x4 *>(&gs[buf][cl][4 * col4]) = g;
+            }
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
+
+    const int stages = C / kLcKc;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int s = 0; s < stages; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < stages) load_stage(s + 1);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int shift = H + (t - 1) * d;
+#pragma unroll
+            for (int kk = 0; kk < kLcKc / 2; ++kk) {
+                const int kr = 2 * kk + h;
+                float av[2], bv[2];
+#pragma unroll
+                for (int tc = 0; tc < 2; ++tc)
+                    av[tc] = ws[buf][t * kLcKc + kr][(wc * 64 + 32 * tc + i) ^ (32 * h)];
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) bv[tp] = gs[buf][kr][shift + wp * 64 + 32 * tp + i];
+#pragma unroll
+                for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+                    for (int tp = 0; tp < 2; ++tp)
+                        acc[tc][tp] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[tc], bv[tp],
+                                                                          acc[tc][tp], 0, 0, 0);
+            }
+        }
+        if (s + 1 < stages) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: + conv bias + the input itself, one store per value ----
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            const int pos = j0 + wp * 64 + 32 * tp + i;
+            if (pos < L) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int co = co0 + wc * 64 + 32 * tc + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const size_t o = ((size_t)b * C + co) * L + pos;
+                    out[o] = acc[tc][tp][r] + conv_b[co] + x[o];
+                }
+            }
+        }
+}
+
+}  // namespace lgn

@@ -29,7 +29,7 @@ hipError_t launch_swish_gn_hardswish_f32(const float *y, const float *gamma, con
     if (blocks > 0x7fffffffLL || parts > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (cg > 8192) return hipErrorInvalidValue;   // rejected by the API before any launch
     float2 *part = reinterpret_cast<float2 *>(workspace);
-    hipError_t e = launch_kernel(lgn_sgh_stats_kernel, dim3((unsigned)blocks), dim3(kSghThreads),
+    hipError_t e = launch_kernel(lgn_sgh_stats_kernel<true>, dim3((unsigned)blocks), dim3(kSghThreads),
                                  stream, y, C, S, G, (int)parts, 0LL, part);
     if (e != hipSuccess) return e;
     const float2 *cpart = part;

@@ -97,7 +97,10 @@ struct SghSplit {
 constexpr int kSghVec = kSghPerThread / 4;   // float4s per thread per chunk
 
 // Stats kernel: grid = (groups of this round) * parts, starting at group
-// g_first.  part[group * parts + p] = (mean, M2).
+// g_first.  part[group * parts + p] = (mean, M2) of Swish(y), or of y itself
+// with SWISH = false (the LayerNorm statistics of the conv block: one group of
+// C*L values per sample).
+template <bool SWISH = true>
 __global__ __launch_bounds__(kSghThreads) void lgn_sgh_stats_kernel(
     const float *__restrict__ y, int C, long long S, int G, int parts, long long g_first,
     float2 *__restrict__ part) {
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(kSghThreads) void lgn_sgh_stats_kernel(
         v[k] = f < nb4 ? body[f] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const long long ei = sp.edge(tid);
-    const float ev = ei >= 0 ? swish(y[ei]) : 0.f;
+    const float ev = ei >= 0 ? (SWISH ? swish(y[ei]) : y[ei]) : 0.f;
     float sum = ei >= 0 ? ev : 0.f;
     int mine = ei >= 0 ? 1 : 0;
 #pragma unroll
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(kSghThreads) void lgn_sgh_stats_kernel(
         const bool ok = tid + k * kSghThreads < nb4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            v[k][j] = ok ? swish(v[k][j]) : 0.f;
+            v[k][j] = ok ? (SWISH ? swish(v[k][j]) : v[k][j]) : 0.f;
             sum += v[k][j];
         }
         mine += ok ? 4 : 0;

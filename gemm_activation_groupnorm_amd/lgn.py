@@ -41,6 +41,8 @@ EXPORTS = (
     "lgn_linear_lse_bf16",
     "lgn_sgh_workspace_bytes",
     "lgn_swish_gn_hardswish_f32",
+    "lgn_lnconv_workspace_bytes",
+    "lgn_ln_gelu_conv1d_f32",
     "lgn_status_string",
     "lgn_version",
     "lgn_last_hip_error_string",
@@ -91,6 +93,8 @@ def _load():
         ("lgn_sgh_workspace_bytes", [i, i, ctypes.c_longlong, i], sz),
         ("lgn_swish_gn_hardswish_f32",
          [vp, vp, vp, i, i, ctypes.c_longlong, i, f, vp, vp, sz, vp], i),
+        ("lgn_lnconv_workspace_bytes", [i, i, i], sz),
+        ("lgn_ln_gelu_conv1d_f32", [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp], i),
         ("lgn_status_string", [i], ctypes.c_char_p),
         ("lgn_version", [], ctypes.c_char_p),
         ("lgn_last_hip_error_string", [], ctypes.c_char_p),
@@ -214,6 +218,18 @@ def lgn_swish_gn_hardswish_f32(y, gamma, beta, Nb, C, S, G, eps, out, workspace,
                                            Nb, C, S, G, eps, _ptr(out, "f32"),
                                            _ptr(workspace, None), workspace_bytes,
                                            _stream(stream))
+
+
+def lgn_lnconv_workspace_bytes(B: int, C: int, L: int) -> int:
+    return _lib.lgn_lnconv_workspace_bytes(B, C, L)
+
+
+def lgn_ln_gelu_conv1d_f32(x, ln_w, ln_b, conv_w, conv_b, B, C, L, dilation, eps, gelu_tanh, out,
+                           workspace, workspace_bytes, stream=None) -> int:
+    return _lib.lgn_ln_gelu_conv1d_f32(_ptr(x, "f32"), _ptr(ln_w, "f32"), _ptr(ln_b, "f32"),
+                                       _ptr(conv_w, "f32"), _ptr(conv_b, "f32"), B, C, L,
+                                       dilation, eps, int(bool(gelu_tanh)), _ptr(out, "f32"),
+                                       _ptr(workspace, None), workspace_bytes, _stream(stream))
 
 
 def lgn_status_string(status: int) -> str:

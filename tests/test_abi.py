@@ -251,3 +251,49 @@ def test_wide_unsupported(fn, bad):
 @pytest.mark.parametrize("fn", WIDE_FNS, ids=lambda f: f.__name__)
 def test_wide_empty_batch_is_a_no_op(fn):
     assert _call_wide(fn, M=0, x=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK
+
+
+# ---- LayerNorm -> GELU -> dilated Conv1d -> + input ----
+
+LNC_GOOD = dict(B=2, C=256, L=4096, d=4, eps=1e-5, tanh=0)
+
+
+def _call_lnc(**kw):
+    a = dict(x=A, ln_w=A, ln_b=A, conv_w=A, conv_b=A, out=A + 4096, ws=A, ws_bytes=1 << 40,
+             **LNC_GOOD)
+    a.update(kw)
+    return lgn.lgn_ln_gelu_conv1d_f32(a["x"], a["ln_w"], a["ln_b"], a["conv_w"], a["conv_b"],
+                                      a["B"], a["C"], a["L"], a["d"], a["eps"], a["tanh"],
+                                      a["out"], a["ws"], a["ws_bytes"], stream=0)
+
+
+def test_lnconv_workspace_bytes():
+    # packed weights 3*C*C floats (256-byte padded), then one (mean, M2) pair
+    # per 16384-value chunk of each sample
+    assert lgn.lgn_lnconv_workspace_bytes(32, 256, 4096) == 3 * 256 * 256 * 4 + 32 * 64 * 8
+    assert lgn.lgn_lnconv_workspace_bytes(1, 128, 4) == 3 * 128 * 128 * 4 + 1 * 1 * 8
+    assert lgn.lgn_lnconv_workspace_bytes(0, 128, 4) == 0
+
+
+LNC_INVALID = [dict(B=-1), dict(C=0), dict(L=0), dict(d=0), dict(eps=0.0), dict(eps=math.inf),
+               dict(x=None), dict(ln_w=None), dict(ln_b=None), dict(conv_w=None),
+               dict(conv_b=None), dict(out=None), dict(ws=None), dict(out=A),
+               dict(ws_bytes=lgn.lgn_lnconv_workspace_bytes(2, 256, 4096) - 1)]
+LNC_UNSUPPORTED = [dict(C=192), dict(L=4094), dict(d=17), dict(x=A + 4), dict(ln_w=A + 8),
+                   dict(ln_b=A + 4), dict(out=A + 4100), dict(ws=A + 8), dict(conv_w=A + 2),
+                   dict(C=1 << 16, L=1 << 16)]
+
+
+@pytest.mark.parametrize("bad", LNC_INVALID, ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_lnconv_invalid_arguments(bad):
+    assert _call_lnc(**bad) == lgn.LGN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", LNC_UNSUPPORTED,
+                         ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_lnconv_unsupported(bad):
+    assert _call_lnc(**bad) == lgn.LGN_ERR_UNSUPPORTED
+
+
+def test_lnconv_empty_batch_is_a_no_op():
+    assert _call_lnc(B=0, x=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK
