@@ -51,6 +51,7 @@ KERNEL_SOURCES = {
     "wide": ("lgn_device.hpp", "lgn_fused.hpp", "lgn_wide.hpp", "lgn_wide_impl.hpp",
              "lgn_wide_f32.hip", "lgn_wide_bf16.hip"),
     "lse": ("lgn_device.hpp", "lgn_lse.hpp", "lgn_lse.hip"),
+    "lnconv": ("lgn_device.hpp", "lgn_sgh.hpp", "lgn_lnconv.hpp", "lgn_lnconv.hip"),
     "sgh": ("lgn_device.hpp", "lgn_sgh.hpp", "lgn_sgh.hip"),
 }
 
@@ -262,6 +263,76 @@ class SghRunner(_Timed):
         return float(np.max(np.abs(y - ref))), len(rows)
 
 
+class LnConvRunner(_Timed):
+    """LayerNorm -> GELU -> dilated Conv1d -> + input on x [B, C, L], resident."""
+
+    def __init__(self, w):
+        import numpy as np
+        import torch
+        from gemm_activation_groupnorm_amd import lgn
+        from gemm_activation_groupnorm_amd.inputs import make_lnconv_inputs
+
+        self.w, self.variant = w, "lnconv"
+        t0 = time.perf_counter()
+        self.inp = make_lnconv_inputs(w.B, w.C, w.L, w.seed)
+        self.d = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda:0")
+                  for k, v in self.inp.items()}
+        self.out = torch.empty_like(self.d["x"])
+        nb = lgn.lgn_lnconv_workspace_bytes(w.B, w.C, w.L)
+        self.ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device="cuda:0")
+        torch.cuda.synchronize()
+        eprint("[bench] %s/lnconv inputs ready in %.1f s" % (w.name, time.perf_counter() - t0))
+        self.stream = torch.cuda.current_stream()
+        d, s = self.d, self.stream
+        args = (d["x"], d["ln_w"], d["ln_b"], d["conv_w"], d["conv_b"], w.B, w.C, w.L, w.dilation,
+                w.eps, w.gelu_tanh, self.out, self.ws, nb)
+        self.launch = lambda: lgn.check(lgn.lgn_ln_gelu_conv1d_f32(*args, stream=s))
+
+    def check_rows(self, ncols: int = 16):
+        """Max abs error against the oracle on `ncols` sampled output columns (b, :, j)."""
+        import numpy as np
+        import oracle
+        r = np.random.default_rng(99)
+        w = self.w
+        cols = [(int(b), int(j)) for b, j in zip(r.integers(0, w.B, ncols), r.integers(0, w.L, ncols))]
+        ref = oracle.ln_gelu_conv1d_cols(self.inp["x"], self.inp["ln_w"], self.inp["ln_b"],
+                                         self.inp["conv_w"], self.inp["conv_b"], w.dilation, w.eps,
+                                         cols, gelu_tanh=w.gelu_tanh)
+        y = np.stack([self.out[b, :, j].cpu().numpy() for b, j in cols]).astype(np.float64)
+        return float(np.max(np.abs(y - ref))), len(cols)
+
+
+def lnconv_main(args):
+    """One JSON line for the LayerNorm -> GELU -> dilated Conv1d -> + input path
+    (three launches per step), as convolution TFLOP/s."""
+    from gemm_activation_groupnorm_amd.inputs import LNCONV_WORKLOADS
+    w = [x for x in LNCONV_WORKLOADS if x.name == args.workload]
+    if not w:
+        raise SystemExit("--variant lnconv needs one of: %s" % [x.name for x in LNCONV_WORKLOADS])
+    w = w[0]
+    r = LnConvRunner(w)
+    wall, kmean = r.time(args.steps, args.warmup)
+    ach = w.flops / (kmean * 1e-3) / 1e12
+    err, ncols = r.check_rows()
+    eprint("[bench] %s/lnconv: %.3f ms/step, kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f); "
+           "sampled-column max err %.2e" % (w.name, wall / args.steps * 1e3, kmean, ach,
+                                            100 * ach / PEAK_TFLOPS["f32"], PEAK_TFLOPS["f32"], err))
+    print(json.dumps({
+        "metric": "LayerNorm->GELU->dilated Conv1d->+x convolution TFLOP/s", "value": round(
+            w.flops / (wall / args.steps) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "C": w.C, "L": w.L, "dilation": w.dilation,
+                   "eps": w.eps, "gelu": "tanh" if w.gelu_tanh else "exact", "seed": w.seed,
+                   "variant": "lnconv"},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_TFLOPS["f32"],
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS["f32"], 4),
+                     "traffic": traffic_for(w.name, "lnconv"), "kernel_ms_mean": round(kmean, 4),
+                     "kernel": "wpack+stats+lnconv"},
+        "check": {"columns": ncols, "max_abs_err_vs_oracle": err}}), flush=True)
+
+
 def torch_context(w):
     """Context only: torch's linear (vendor GEMM, output in the input type) and
     the unfused torch pipeline (linear, SiLU, add, group_norm) on random
@@ -358,7 +429,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", default="fused",
-                    choices=["fused", "twopass", "wide", "lse", "sgh"],
+                    choices=["fused", "twopass", "wide", "lse", "sgh", "lnconv"],
                     help="lse: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 (use with an "
                          "m1024_k8192_n8192_lse_* workload); sgh: Swish -> spatial GroupNorm -> "
                          "HardSwish (use with an *_sgh_* workload; reports GB/s)")
@@ -414,6 +485,9 @@ def main():
 
     if args.variant == "sgh":
         sgh_main(args)
+        return
+    if args.variant == "lnconv":
+        lnconv_main(args)
         return
     w = get_workload(args.workload)
     r = Runner(w, args.variant)
@@ -516,6 +590,23 @@ def main():
                           "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                           "max_abs_err_vs_oracle": e2})
             del rs
+            torch.cuda.empty_cache()
+        from gemm_activation_groupnorm_amd.inputs import LNCONV_WORKLOADS
+        for wl_ in LNCONV_WORKLOADS:
+            rl = LnConvRunner(wl_)
+            n_extra = 30
+            wl, km_mean = rl.time(n_extra, 3, min_warm_ms=100.0)
+            ach = wl_.flops / (km_mean * 1e-3) / 1e12
+            e2, _ = rl.check_rows(8)
+            eprint("[bench] %s/lnconv: kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f), "
+                   "err %.2e" % (wl_.name, km_mean, ach, 100 * ach / PEAK_TFLOPS["f32"],
+                                 PEAK_TFLOPS["f32"], e2))
+            extra.append({"workload": wl_.name, "variant": "lnconv", "dtype": "f32",
+                          "ms_per_step": round(wl / n_extra * 1e3, 4),
+                          "kernel_ms_mean": round(km_mean, 4), "tflops": round(ach, 3),
+                          "frac_of_peak": round(ach / PEAK_TFLOPS["f32"], 4),
+                          "max_abs_err_vs_oracle": e2})
+            del rl
             torch.cuda.empty_cache()
         res["extra"] = extra
 

@@ -26,14 +26,24 @@
 
 namespace lgn {
 
-constexpr int kLcCo = 128;        // output channels per workgroup
-constexpr int kLcPos = 128;       // positions per workgroup
 constexpr int kLcKc = 16;         // input channels per stage (K = 3 * 16 per stage)
-constexpr int kLcThreads = 256;   // 4 waves: 2 (channels) x 2 (positions) of 64 x 64
 constexpr int kLcMaxHalo = 16;    // largest dilation handled (halo rounded up to 4)
-constexpr int kLcGP = kLcPos + 2 * kLcMaxHalo;   // LDS pitch of an activation row
-constexpr int kLcWf4 = 3 * kLcKc * kLcCo / 4 / kLcThreads;                 // weight float4s per thread
-constexpr int kLcGf4 = (kLcKc * kLcGP / 4 + kLcThreads - 1) / kLcThreads;  // activation float4s, at most
+
+// Workgroup tile: CO output channels x POS positions; waves of 64 channels x
+// WPOS positions, (CO / 64) x (POS / WPOS) of them.
+template <int CO_, int POS_, int WPOS_>
+struct LcTile {
+    static constexpr int CO = CO_, POS = POS_, WPOS = WPOS_;
+    static constexpr int WAVES_C = CO / 64, WAVES_P = POS / WPOS;
+    static constexpr int NT = 64 * WAVES_C * WAVES_P;
+    static constexpr int TP = WPOS / 32;                       // 32-position MFMA tiles per wave
+    static constexpr int GP = POS + 2 * kLcMaxHalo;            // LDS pitch of an activation row
+    static constexpr int WF4 = 3 * kLcKc * CO / 4 / NT;        // weight float4s per thread
+    static constexpr int GF4 = 3;                              // activation float4s per thread
+    static_assert(WF4 == 6, "six weight float4s per thread and stage");
+};
+typedef LcTile<128, 128, 64> LcSmall;    // 4 waves of 64 x 64
+typedef LcTile<256, 256, 128> LcLarge;   // 8 waves of 64 x 128
 
 // W [co][ci][t] -> Wt [t][ci][co]: the weights as K-major rows of output
 // channels, so a stage's weight slab is read with 16-byte loads.
@@ -60,27 +70,36 @@ __device__ __forceinline__ float lc_gelu(float v) {
 }
 
 // The convolution with LayerNorm + GELU applied while staging.  Grid: one
-// workgroup per (sample, 128-position tile, 128-channel tile), channel tiles
-// fastest; the hardware id is remapped so each XCD gets a contiguous run.
+// workgroup per (sample, position tile, channel tile), channel tiles fastest;
+// the hardware id is remapped so each XCD gets a contiguous run.
 // part[b * parts + p] = (mean, M2) of chunk p (kSghChunk values) of sample b.
-// H = the dilation rounded up to a multiple of 4 (<= kLcMaxHalo).
-// Requires C % 128 == 0, L % 4 == 0, 1 <= d <= H <= 16; out must not overlap x.
-template <bool TANH>
-__global__ __launch_bounds__(kLcThreads) void lgn_lnconv_kernel(
+// H = the staged halo: the dilation rounded up to a multiple of 4 (<= kLcMaxHalo).
+// Requires C % Tile::CO == 0, L % 4 == 0, 1 <= d <= H <= 16; out must not overlap x.
+// The next stage's weights and activations are loaded at the top of a stage
+// and written to the other LDS buffer in three parts, one after each tap's
+// MFMAs, so that their LayerNorm + GELU arithmetic runs under the MFMAs.
+template <class Tile, bool TANH, int H>
+__global__ __launch_bounds__(Tile::NT) void lgn_lnconv_kernel(
     const float *__restrict__ x, const float *__restrict__ ln_w, const float *__restrict__ ln_b,
     const float *__restrict__ wt, const float *__restrict__ conv_b,
-    const float2 *__restrict__ part, int C, int L, int d, int H, int parts, float eps,
+    const float2 *__restrict__ part, int C, int L, int d, int parts, float eps,
     int tiles_l, int tiles_c, float *__restrict__ out) {
+    constexpr int CO = Tile::CO, POS = Tile::POS, NT = Tile::NT, TP = Tile::TP;
+    constexpr int WF4 = Tile::WF4, GF4 = Tile::GF4, GP = Tile::GP;
+    static_assert(H % 4 == 0 && H >= 4 && H <= kLcMaxHalo, "halo: 4, 8, 12 or 16");
+    constexpr int win4 = (POS + 2 * H) / 4;   // float4s per staged activation row
+    constexpr int gtot = kLcKc * win4;
+    static_assert(gtot > (GF4 - 1) * NT && gtot <= GF4 * NT, "three activation float4s per thread");
     // weight rows: odd rows have their 32-float halves swapped (column ^ 32),
     // so the two lane halves of a read (rows 2k, 2k+1) hit disjoint banks
-    __shared__ __attribute__((aligned(16))) float ws[2][3 * kLcKc][kLcCo];
-    __shared__ __attribute__((aligned(16))) float gs[2][kLcKc][kLcGP];
-    __shared__ float red[3 * (kLcThreads / 64)];
+    __shared__ __attribute__((aligned(16))) float ws[2][3 * kLcKc][CO];
+    __shared__ __attribute__((aligned(16))) float gs[2][kLcKc][GP];
+    __shared__ float red[3 * (NT / 64)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int i = lane & 31, h = lane >> 5;
-    const int wc = wave & 1, wp = wave >> 1;
+    const int wc = wave % Tile::WAVES_C, wp = wave / Tile::WAVES_C;
 
     const int nblocks = gridDim.x;
     int t_id = blockIdx.x;
@@ -89,42 +108,40 @@ __global__ __launch_bounds__(kLcThreads) void lgn_lnconv_kernel(
     const int rest = t_id / tiles_c;
     const int lt = rest % tiles_l;
     const int b = rest / tiles_l;
-    const int co0 = ct * kLcCo;
-    const int j0 = lt * kLcPos;
+    const int co0 = ct * CO;
+    const int j0 = lt * POS;
 
     // ---- the sample's statistics from its chunk partials, in a fixed order ----
     const long long n = (long long)C * L;
     float mean = 0.f, m2 = 0.f, cnt = 0.f;
-    for (int t = tid; t < parts; t += kLcThreads) {
+    for (int t = tid; t < parts; t += NT) {
         const long long ctn = n - (long long)t * kSghChunk;
         const float2 q = part[(size_t)b * parts + t];
         chan_merge(mean, m2, cnt, q.x, q.y, (float)(ctn < kSghChunk ? ctn : kSghChunk));
     }
-    block_merge(mean, m2, cnt, red);
+    block_merge<NT / 64>(mean, m2, cnt, red);
     const float rstd = __builtin_amdgcn_rsqf(m2 / (float)n + eps);
     const float nmr = -mean * rstd;
 
     const float *xb = x + (size_t)b * C * L;
-    const int win4 = (kLcPos + 2 * H) / 4;        // float4s per staged activation row
-    const int gtot = kLcKc * win4;
 
-    f32x4 rw[kLcWf4];
-    f32x4 rx[kLcGf4], rg[kLcGf4], rb[kLcGf4];
+    f32x4 rw[WF4];
+    f32x4 rx[GF4], rg[GF4], rb[GF4];
 
     // global -> registers for stage s (input channels s*16 .. s*16+15)
     auto load_stage = [&](int s) {
         const int c0 = s * kLcKc;
 #pragma unroll
-        for (int q = 0; q < kLcWf4; ++q) {
-            const int f = tid + q * kLcThreads;
-            const int row = f >> 5, col4 = f & 31;     // row = t * 16 + cl
+        for (int q = 0; q < WF4; ++q) {
+            const int f = tid + q * NT;
+            const int row = f / (CO / 4), col4 = f % (CO / 4);   // row = t * 16 + cl
             const int t = row / kLcKc, cl = row % kLcKc;
             rw[q] = *reinterpret_cast<const f32x4 *>(
                 wt + ((size_t)(t * C + c0 + cl) * C + co0 + 4 * col4));
         }
 #pragma unroll
-        for (int q = 0; q < kLcGf4; ++q) {
-            const int f = tid + q * kLcThreads;
+        for (int q = 0; q < GF4; ++q) {
+            const int f = tid + q * NT;
             const int cl = f / win4, col4 = f - cl * win4;
             const int p = j0 - H + 4 * col4;
             if (f < gtot && p >= 0 && p < L) {
@@ -135,17 +152,22 @@ __global__ __launch_bounds__(kLcThreads) void lgn_lnconv_kernel(
             }
         }
     };
-    // registers -> LDS buffer `buf`, LayerNorm + GELU on the way; 0 outside [0, L)
-    auto store_stage = [&](int buf) {
+    // registers -> LDS buffer `buf`, LayerNorm + GELU on the way; 0 outside [0, L).
+    // Part 0: weight float4s 0-2; part 1: weight float4s 3-5 and activation
+    // float4 0; part 2: activation float4s 1-2 (all of them: part -1).
+    auto store_stage = [&](int buf, int which) {
 #pragma unroll
-        for (int q = 0; q < kLcWf4; ++q) {
-            const int f = tid + q * kLcThreads;
-            const int row = f >> 5;
-            *reinterpret_cast<f32x4 *>(&ws[buf][row][(4 * (f & 31)) ^ (32 * (row & 1))]) = rw[q];
+        for (int q = 0; q < WF4; ++q) {
+            if (which >= 0 && which != (q < 3 ? 0 : 1)) continue;
+            const int f = tid + q * NT;
+            const int row = f / (CO / 4);
+            *reinterpret_cast<f32x4 *>(&ws[buf][row][(4 * (f % (CO / 4))) ^ (32 * (row & 1))]) =
+                rw[q];
         }
 #pragma unroll
-        for (int q = 0; q < kLcGf4; ++q) {
-            const int f = tid + q * kLcThreads;
+        for (int q = 0; q < GF4; ++q) {
+            if (which >= 0 && which != (q == 0 ? 1 : 2)) continue;
+            const int f = tid + q * NT;
             const int cl = f / win4, col4 = f - cl * win4;
             const int p = j0 - H + 4 * col4;
             if (f < gtot) {
@@ -161,42 +183,44 @@ __global__ __launch_bounds__(kLcThreads) void lgn_lnconv_kernel(
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[2][TP];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < TP; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
 
     const int stages = C / kLcKc;
     load_stage(0);
-    store_stage(0);
+    store_stage(0, -1);
     __syncthreads();
     for (int s = 0; s < stages; ++s) {
         const int buf = s & 1;
-        if (s + 1 < stages) load_stage(s + 1);
+        const bool more = s + 1 < stages;
+        if (more) load_stage(s + 1);
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
             const int shift = H + (t - 1) * d;
 #pragma unroll
             for (int kk = 0; kk < kLcKc / 2; ++kk) {
                 const int kr = 2 * kk + h;
-                float av[2], bv[2];
+                float av[2], bv[TP];
 #pragma unroll
                 for (int tc = 0; tc < 2; ++tc)
                     av[tc] = ws[buf][t * kLcKc + kr][(wc * 64 + 32 * tc + i) ^ (32 * h)];
 #pragma unroll
-                for (int tp = 0; tp < 2; ++tp) bv[tp] = gs[buf][kr][shift + wp * 64 + 32 * tp + i];
+                for (int tp = 0; tp < TP; ++tp)
+                    bv[tp] = gs[buf][kr][shift + wp * Tile::WPOS + 32 * tp + i];
 #pragma unroll
                 for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
-                    for (int tp = 0; tp < 2; ++tp)
+                    for (int tp = 0; tp < TP; ++tp)
                         acc[tc][tp] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[tc], bv[tp],
                                                                           acc[tc][tp], 0, 0, 0);
             }
+            if (more) store_stage(buf ^ 1, t);
         }
-        if (s + 1 < stages) store_stage(buf ^ 1);
         __syncthreads();
     }
 
@@ -204,8 +228,8 @@ __global__ __launch_bounds__(kLcThreads) void lgn_lnconv_kernel(
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-            const int pos = j0 + wp * 64 + 32 * tp + i;
+        for (int tp = 0; tp < TP; ++tp) {
+            const int pos = j0 + wp * Tile::WPOS + 32 * tp + i;
             if (pos < L) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {

@@ -49,7 +49,9 @@ __device__ __forceinline__ void chan_merge(float &mean, float &m2, float &n, flo
 
 // Merge across the wave (xor butterfly, lower lane's partial first in each
 // pair, so both lanes of a pair hold the same bits), then across the block's
-// waves through LDS in wave order.  Every thread returns the block's result.
+// WAVES waves through LDS (red: 3 * WAVES floats) in wave order.  Every thread
+// of the block must call it; every thread returns the block's result.
+template <int WAVES = kSghThreads / 64>
 __device__ __forceinline__ void block_merge(float &mean, float &m2, float &n, float *red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -72,7 +74,7 @@ __device__ __forceinline__ void block_merge(float &mean, float &m2, float &n, fl
     m2 = red[1];
     n = red[2];
 #pragma unroll
-    for (int w = 1; w < kSghThreads / 64; ++w) chan_merge(mean, m2, n, red[3 * w], red[3 * w + 1], red[3 * w + 2]);
+    for (int w = 1; w < WAVES; ++w) chan_merge(mean, m2, n, red[3 * w], red[3 * w + 1], red[3 * w + 2]);
 }
 
 // A chunk [start, end) of absolute element indices, split for 16-byte
