@@ -70,8 +70,8 @@ __device__ __forceinline__ float lc_gelu(float v) {
 }
 
 // The convolution with LayerNorm + GELU applied while staging.  Grid: one
-// workgroup per (sample, position tile, channel tile), channel tiles fastest;
-// the hardware id is remapped so each XCD gets a contiguous run.
+// workgroup per (sample, position tile, channel tile), samples fastest; the
+// hardware id is remapped so each XCD gets a contiguous run.
 // part[b * parts + p] = (mean, M2) of chunk p (kSghChunk values) of sample b.
 // H = the staged halo: the dilation rounded up to a multiple of 4 (<= kLcMaxHalo).
 // Requires C % Tile::CO == 0, L % 4 == 0, 1 <= d <= H <= 16; out must not overlap x.
@@ -104,10 +104,14 @@ __global__ __launch_bounds__(Tile::NT) void lgn_lnconv_kernel(
     const int nblocks = gridDim.x;
     int t_id = blockIdx.x;
     if ((nblocks & 7) == 0) t_id = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
-    const int ct = t_id % tiles_c;
-    const int rest = t_id / tiles_c;
-    const int lt = rest % tiles_l;
-    const int b = rest / tiles_l;
+    // samples fastest: the workgroups resident on one XCD at a time cover the
+    // same positions of different samples, so ln_w / ln_b windows (shared by
+    // every sample) and the weights are re-read from that XCD's L2
+    const int nb_ = nblocks / (tiles_c * tiles_l);
+    const int b = t_id % nb_;
+    const int rest = t_id / nb_;
+    const int ct = rest % tiles_c;
+    const int lt = rest / tiles_c;
     const int co0 = ct * CO;
     const int j0 = lt * POS;
 
