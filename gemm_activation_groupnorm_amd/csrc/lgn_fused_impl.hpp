@@ -17,9 +17,10 @@ namespace lgn {
 //               bf16: the CG <= 64 tile, 2 waves per group
 //   CG == 256 : fp32: 128 x 256, 2 x 2 waves of 64 x 128 (2 waves per group), ring of 3;
 //               bf16: the CG <= 64 tile, 4 waves per group
-//   CG == 512 :  64 x 512, 1 x 4 waves of 64 x 128 (4 waves per group), ring of 3
-//   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128 (8 waves per group), ring of 2,
-//                simple schedule (fragments read right before their MFMAs)
+//   CG == 512 : fp32: 64 x 512, 1 x 4 waves of 64 x 128 (4 waves per group), ring of 3;
+//               bf16: 128 x 512, 2 x 4 waves of 64 x 128, ring of 3
+//   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128 (8 waves per group), ring of 2;
+//                fp32 with the simple schedule (fragments read right before their MFMAs)
 // and register-staged tiles for any other K.
 template <class DT, class Cfg, int CG, int RING>
 hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
@@ -73,8 +74,11 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
     typedef typename std::conditional<BF, F64, TileCfg<DT, 256, 128, 4, 1, 64, 2>>::type F128;
     typedef typename std::conditional<BF, F64, TileCfg<DT, 128, 256, 2, 2, 64>>::type F256;
     constexpr int R128 = BF ? 4 : 3;
-    typedef TileCfg<DT, 64, 512, 1, 4, 64> F512;
-    typedef TileCfg<DT, 64, 1024, 1, 8, 64, 1, 0> F1024;   // simple schedule
+    typedef typename std::conditional<BF, TileCfg<DT, 128, 512, 2, 4, 64, 2>,
+                                      TileCfg<DT, 64, 512, 1, 4, 64>>::type F512;
+    // fp32: simple schedule; bf16: fragments read under the MFMAs
+    typedef typename std::conditional<BF, TileCfg<DT, 64, 1024, 1, 8, 64, 1, 1>,
+                                      TileCfg<DT, 64, 1024, 1, 8, 64, 1, 0>>::type F1024;
     const int cg = N / G;
 #define LGN_CASE(C, FAST, RING, SLOW)                                                            \
     case C:                                                                                     \

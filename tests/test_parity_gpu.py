@@ -64,6 +64,8 @@ SHAPES = [
     (520, 192, 1152, 9),    # 128, ragged
     (333, 96, 512, 4),      # 128, 2 groups per 256-channel tile (bf16: 2 waves per group)
     (300, 320, 768, 3),     # 256, 10 bf16 stages (bf16: 4 waves per group), ragged M
+    (130, 64, 1024, 2),     # 512, 2 bf16 stages on the 128 x 512 bf16 tile, ragged M
+    (200, 96, 2048, 2),     # 1024, 3 bf16 stages, ragged M over 64-sample tiles
 ]
 
 
