@@ -54,8 +54,7 @@ struct TileParams {
 // per row and WC-channel span, the (mean, M2) of those WC values to
 // wide_part[row * (N / WC) + span]; a second kernel merges a group's spans and
 // normalises.  The epilogue keeps the per-sample-tile order of the normal
-// path (statistics, then that sample tile's stores), which measured faster
-// than reducing whole tiles across waves before storing.
+// path: statistics, then that sample tile's stores.
 template <class DT, class Cfg, int CG, int RING, bool WIDE = false>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC)))
 void lgn_fused_kernel(
