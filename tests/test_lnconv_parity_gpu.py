@@ -68,6 +68,20 @@ def test_lnconv_zero_weights_give_bias_plus_input_exactly():
     assert np.array_equal(out.cpu().numpy(), want)
 
 
+def test_lnconv_constant_sample():
+    # variance 0: the normalised values are 0 and g = GELU(ln_b) (rstd = 1/sqrt(eps))
+    B, C, L, dil = 2, 256, 260, 3
+    inp = make_lnconv_inputs(B, C, L, 81)
+    inp["x"][1] = 0.75
+    out = run_lnconv(dev(inp), B, C, L, dil)
+    torch.cuda.synchronize()
+    ref = oracle.ln_gelu_conv1d(inp["x"], inp["ln_w"], inp["ln_b"], inp["conv_w"], inp["conv_b"],
+                                dil, 1e-5)
+    err = _err(out.cpu().numpy(), ref)
+    log("  constant sample: max abs err %.3e" % err)
+    assert err <= TOL["f32"]
+
+
 def test_lnconv_deterministic_and_side_stream():
     B, C, L, dil = 2, 256, 512, 4
     inp = make_lnconv_inputs(B, C, L, 78)
