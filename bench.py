@@ -446,6 +446,9 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the forward, run the MFMA-ceiling probe (sustained MFMA rate "
                          "and shader clock for zero and random operands) and exit")
+    ap.add_argument("--lds-bandwidth", action="store_true",
+                    help="instead of the forward, run the LDS-bandwidth probe (16-byte LDS reads, "
+                         "bytes per shader clock per CU) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the forward, run 5 plain device copies of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -459,13 +462,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.mfma_ceiling:
+    if args.mfma_ceiling or args.lds_bandwidth:
         # a child process of its own: this process has not touched the GPU
         import subprocess
         from gemm_activation_groupnorm_amd import build as hip_build
-        if not os.path.exists(hip_build.PROBE):
+        exe = hip_build.PROBE if args.mfma_ceiling else hip_build.LDS_PROBE
+        if not os.path.exists(exe):
             hip_build.build_probe()
-        sys.exit(subprocess.run([hip_build.PROBE]).returncode)
+        sys.exit(subprocess.run([exe]).returncode)
 
     import torch
     if args.copy_calibration:
