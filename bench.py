@@ -449,6 +449,14 @@ def main():
     ap.add_argument("--lds-bandwidth", action="store_true",
                     help="instead of the forward, run the LDS-bandwidth probe (16-byte LDS reads, "
                          "bytes per shader clock per CU) and exit")
+    ap.add_argument("--l2-feed", action="store_true",
+                    help="instead of the forward, run the operand-feed probe (global -> LDS DMA "
+                         "of a 512-row panel with 64- or 128-byte LDS rows, bytes per shader "
+                         "clock per CU) and exit")
+    ap.add_argument("--fused-phases", action="store_true",
+                    help="instead of the forward, run the fused-tile phase probe (shader cycles "
+                         "of the main loop, epilogue and store drain per tile, and the clock) at "
+                         "the pages' shape in bf16 and fp32, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the forward, run 5 plain device copies of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -462,11 +470,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.mfma_ceiling or args.lds_bandwidth:
+    if args.mfma_ceiling or args.lds_bandwidth or args.l2_feed or args.fused_phases:
         # a child process of its own: this process has not touched the GPU
         import subprocess
         from gemm_activation_groupnorm_amd import build as hip_build
-        exe = hip_build.PROBE if args.mfma_ceiling else hip_build.LDS_PROBE
+        exe = (hip_build.PROBE if args.mfma_ceiling else
+               hip_build.LDS_PROBE if args.lds_bandwidth else
+               hip_build.FEED_PROBE if args.l2_feed else hip_build.PHASES_PROBE)
         if not os.path.exists(exe):
             hip_build.build_probe()
         sys.exit(subprocess.run([exe]).returncode)

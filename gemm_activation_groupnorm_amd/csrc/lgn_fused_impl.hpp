@@ -33,7 +33,8 @@ hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     return launch_kernel(lgn_fused_kernel<DT, Cfg, CG, RING>, dim3((unsigned)blocks),
                          dim3(Cfg::NT), stream, x, W, b_lin, b_add, gamma, beta, M, K, N, eps,
-                         out, tiles_m, tiles_n, (float2 *)nullptr);
+                         out, tiles_m, tiles_n, (float2 *)nullptr,
+                         (unsigned long long *)nullptr);
 }
 
 // The LDS DMA ring needs K to be a multiple of its stage depth; any other K

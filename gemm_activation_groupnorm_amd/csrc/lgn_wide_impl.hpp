@@ -31,13 +31,13 @@ hipError_t launch_wide(const typename dt_traits<DT>::storage *x,
         e = launch_kernel(lgn_fused_kernel<DT, Fast, kWideSpan, RING, true>,
                           dim3((unsigned)((long long)tiles_m * tiles_n)), dim3(Fast::NT), stream,
                           x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, tiles_m, tiles_n,
-                          part);
+                          part, (unsigned long long *)nullptr);
     } else {
         const int tiles_m = (M + Slow::BS - 1) / Slow::BS;
         e = launch_kernel(lgn_fused_kernel<DT, Slow, kWideSpan, 0, true>,
                           dim3((unsigned)((long long)tiles_m * tiles_n)), dim3(Slow::NT), stream,
                           x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, tiles_m, tiles_n,
-                          part);
+                          part, (unsigned long long *)nullptr);
     }
     if (e != hipSuccess) return e;
     const long long pairs = (long long)M * G;

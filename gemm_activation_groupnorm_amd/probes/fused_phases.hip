@@ -1,0 +1,146 @@
+// fused_phases.hip -- where the cycles of one fused tile go.
+//
+// Instantiates the fused kernel with its PHASES hook on (lgn_fused.hpp) for
+// the C <= 64 entries of the tile table in lgn_fused_impl.hpp (256 x 256
+// tiles, 2 x 4 waves of 128 x 64; bf16 on a 4-stage DMA ring with the
+// mid-stage barrier, fp32 on a 3-stage ring) and runs it at the pages' shape,
+// M = 32768, K = 1024, N = 4096, G = 64, on random inputs with the workload's
+// distributions.  Lane 0 of every wave records the shader clock at entry,
+// after the main loop, after the epilogue has issued its stores and after the
+// stores have completed, and the real-time clock at entry and exit.
+//
+// Output, one JSON object per dtype: kernel time (mean over 20 launches after
+// 300 ms of warm-up), the shader clock during the kernel, and per 256 x 256
+// tile the median cycles of the main loop (incl. the ring prologue), the
+// epilogue and the store drain, next to the cycles the tile's MFMAs alone take
+// at the dense rate (bf16: 1024 FLOP per clock per SIMD, fp32: 64).
+// Not part of liblgn.so; built next to it by gemm_activation_groupnorm_amd.build.
+#include "../csrc/lgn_fused_impl.hpp"
+
+#include <algorithm>
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <random>
+#include <vector>
+
+using namespace lgn;
+
+#define CHECK(x)                                                                         \
+    do {                                                                                 \
+        hipError_t e_ = (x);                                                             \
+        if (e_ != hipSuccess) {                                                          \
+            fprintf(stderr, "HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+            return 1;                                                                    \
+        }                                                                                \
+    } while (0)
+
+static uint16_t to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    u += 0x7fff + ((u >> 16) & 1);
+    return (uint16_t)(u >> 16);
+}
+
+static double median(std::vector<double> v) {
+    std::sort(v.begin(), v.end());
+    return v.empty() ? 0.0 : v[v.size() / 2];
+}
+
+template <class DT, class Cfg, int RING>
+static int run(const char *name, double flop_per_clk_simd) {
+    typedef typename dt_traits<DT>::storage T;
+    const int M = 32768, K = 1024, N = 4096, G = 64;
+    const float eps = 1e-5f;
+    std::mt19937 gen(7);
+    std::normal_distribution<float> nd(0.f, 1.f);
+    std::uniform_real_distribution<float> ud(-1.f / 32.f, 1.f / 32.f);
+    std::vector<T> hx((size_t)M * K), hw((size_t)N * K);
+    for (auto &v : hx) {
+        const float f = nd(gen);
+        if constexpr (sizeof(T) == 2) v = to_bf16(f); else v = f;
+    }
+    for (auto &v : hw) {
+        const float f = ud(gen);
+        if constexpr (sizeof(T) == 2) v = to_bf16(f); else v = f;
+    }
+    std::vector<float> hv(4 * (size_t)N);
+    for (int n = 0; n < N; ++n) {
+        hv[n] = ud(gen);
+        hv[N + n] = 0.02f * nd(gen);
+        hv[2 * N + n] = 1.f + 0.1f * nd(gen);
+        hv[3 * N + n] = 0.1f * nd(gen);
+    }
+    T *x, *W;
+    float *vec, *out;
+    unsigned long long *clk;
+    const int tiles_m = M / Cfg::BS, tiles_n = N / Cfg::BC, blocks = tiles_m * tiles_n;
+    const int waves = Cfg::NT / 64;
+    CHECK(hipMalloc(&x, hx.size() * sizeof(T)));
+    CHECK(hipMalloc(&W, hw.size() * sizeof(T)));
+    CHECK(hipMalloc(&vec, hv.size() * sizeof(float)));
+    CHECK(hipMalloc(&out, (size_t)M * N * sizeof(float)));
+    CHECK(hipMalloc(&clk, (size_t)blocks * waves * 6 * sizeof(unsigned long long)));
+    CHECK(hipMemcpy(x, hx.data(), hx.size() * sizeof(T), hipMemcpyHostToDevice));
+    CHECK(hipMemcpy(W, hw.data(), hw.size() * sizeof(T), hipMemcpyHostToDevice));
+    CHECK(hipMemcpy(vec, hv.data(), hv.size() * sizeof(float), hipMemcpyHostToDevice));
+    CHECK(hipMemset(clk, 0, (size_t)blocks * waves * 6 * sizeof(unsigned long long)));
+    auto launch = [&](unsigned long long *pc) {
+        return launch_kernel(lgn_fused_kernel<DT, Cfg, 64, RING, false, true>,
+                             dim3((unsigned)blocks), dim3(Cfg::NT), (hipStream_t)0,
+                             (const T *)x, (const T *)W, (const float *)vec,
+                             (const float *)(vec + N), (const float *)(vec + 2 * N),
+                             (const float *)(vec + 3 * N), M, K, N, eps, out, tiles_m, tiles_n,
+                             (float2 *)nullptr, pc);
+    };
+    // warm the clocks for 300 ms
+    const auto t_end = std::chrono::steady_clock::now() + std::chrono::milliseconds(300);
+    while (std::chrono::steady_clock::now() < t_end) {
+        for (int i = 0; i < 20; ++i) CHECK(launch(clk));
+        CHECK(hipDeviceSynchronize());
+    }
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    CHECK(hipEventRecord(e0));
+    for (int i = 0; i < 20; ++i) CHECK(launch(clk));
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    ms /= 20;
+    std::vector<unsigned long long> hc((size_t)blocks * waves * 6);
+    CHECK(hipMemcpy(hc.data(), clk, hc.size() * sizeof(unsigned long long),
+                    hipMemcpyDeviceToHost));
+    std::vector<double> main_loop, epi, drain, ghz;
+    for (int b = 0; b < blocks; ++b)
+        for (int w = 0; w < waves; ++w) {
+            const unsigned long long *p = &hc[((size_t)b * waves + w) * 6];
+            main_loop.push_back((double)(p[1] - p[0]));
+            epi.push_back((double)(p[2] - p[1]));
+            drain.push_back((double)(p[3] - p[2]));
+            ghz.push_back((double)(p[3] - p[0]) / ((double)(p[5] - p[4]) * 10.0));
+        }
+    const double ideal = 2.0 * Cfg::BS * Cfg::BC * K / (4.0 * flop_per_clk_simd);
+    printf("{\"dtype\": \"%s\", \"workload\": \"m%d_k%d_n%d_g%d\", \"kernel_ms\": %.4f, "
+           "\"tflops\": %.1f, \"shader_clock_ghz\": %.3f, \"tile\": \"%dx%d\", "
+           "\"cycles_main_loop\": %.0f, \"cycles_epilogue\": %.0f, \"cycles_store_drain\": %.0f, "
+           "\"cycles_mfma_only\": %.0f}\n",
+           name, M, K, N, G, ms, 2.0 * M * N * K / ms / 1e9, median(ghz), Cfg::BS, Cfg::BC,
+           median(main_loop), median(epi), median(drain), ideal);
+    fflush(stdout);
+    CHECK(hipFree(x));
+    CHECK(hipFree(W));
+    CHECK(hipFree(vec));
+    CHECK(hipFree(out));
+    CHECK(hipFree(clk));
+    CHECK(hipEventDestroy(e0));
+    CHECK(hipEventDestroy(e1));
+    return 0;
+}
+
+int main() {
+    if (run<bf16_t, TileCfg<bf16_t, 256, 256, 2, 4, 64, 2, 2, 2>, 4>("bf16", 1024.0)) return 1;
+    if (run<f32_t, TileCfg<f32_t, 256, 256, 2, 4, 64, 2>, 3>("f32", 64.0)) return 1;
+    return 0;
+}
