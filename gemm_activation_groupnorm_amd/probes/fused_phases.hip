@@ -1,19 +1,19 @@
 // fused_phases.hip -- where the cycles of one fused tile go.
 //
 // Instantiates the fused kernel with its PHASES hook on (lgn_fused.hpp) for
-// the C <= 64 entries of the tile table in lgn_fused_impl.hpp (256 x 256
-// tiles, 2 x 4 waves of 128 x 64; bf16 on a 4-stage DMA ring with the
-// mid-stage barrier, fp32 on a 3-stage ring) and runs it at the pages' shape,
+// the bf16 C <= 64 entry of the tile table in lgn_fused_impl.hpp (256 x 256
+// tiles, 2 x 4 waves of 128 x 64, a 4-stage DMA ring with the mid-stage
+// barrier) and runs it at the pages' shape,
 // M = 32768, K = 1024, N = 4096, G = 64, on random inputs with the workload's
 // distributions.  Lane 0 of every wave records the shader clock at entry,
 // after the main loop, after the epilogue has issued its stores and after the
 // stores have completed, and the real-time clock at entry and exit.
 //
-// Output, one JSON object per dtype: kernel time (mean over 20 launches after
+// Output, one JSON object: kernel time (mean over 20 launches after
 // 300 ms of warm-up), the shader clock during the kernel, and per 256 x 256
 // tile the median cycles of the main loop (incl. the ring prologue), the
 // epilogue and the store drain, next to the cycles the tile's MFMAs alone take
-// at the dense rate (bf16: 1024 FLOP per clock per SIMD, fp32: 64).
+// at the dense rate (1024 bf16 FLOP per clock per SIMD).
 // Not part of liblgn.so; built next to it by gemm_activation_groupnorm_amd.build.
 #include "../csrc/lgn_fused_impl.hpp"
 
@@ -139,8 +139,13 @@ static int run(const char *name, double flop_per_clk_simd) {
     return 0;
 }
 
+// bf16 only: with the hook compiled in, the fp32 instantiation runs about 35 %
+// slower than without it (2.66-2.69 ms against 1.97 ms at this shape, in this
+// probe's code object and in another that also holds the library's kernels;
+// not a matter of loop alignment, which moves it by 3 %), so its phase cycles
+// would not describe the library's fp32 kernel.  The bf16 instantiation runs
+// as fast with the hook as without it.
 int main() {
     if (run<bf16_t, TileCfg<bf16_t, 256, 256, 2, 4, 64, 2, 2, 2>, 4>("bf16", 1024.0)) return 1;
-    if (run<f32_t, TileCfg<f32_t, 256, 256, 2, 4, 64, 2>, 3>("f32", 64.0)) return 1;
     return 0;
 }
