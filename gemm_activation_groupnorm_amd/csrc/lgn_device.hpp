@@ -603,7 +603,9 @@ struct CoreSel<DT, Cfg, 0> {
 // conflict-free both ways for rows of 64..256 channels) and reads it back
 // row by row, so each store instruction writes WC*4 contiguous bytes per row.
 // value(tc, q) gives the lane's 4 channels 32*tc + 8*q + 4*h .. +3 of its row.
-template <int WC>
+// STREAM: non-temporal stores, for output nothing in the kernel reads again:
+// the lines then do not displace the GEMM operands cached in L2 and the MALL.
+template <int WC, bool STREAM = false>
 struct BlockStore {
     static_assert(WC >= 64 && WC <= 256, "block rows of 64..256 channels");
     static constexpr int BYTES = 32 * WC * 4;
@@ -630,7 +632,13 @@ struct BlockStore {
                                                              16 * (chunk ^ (row & 15)));
             const int m = row0 + row;
             const int c = col0 + 4 * chunk;
-            if (m < M && c < N) *reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + c) = y;
+            if (m < M && c < N) {
+                f32x4 *dst = reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + c);
+                if constexpr (STREAM)
+                    __builtin_nontemporal_store(y, dst);
+                else
+                    *dst = y;
+            }
         }
     }
 };

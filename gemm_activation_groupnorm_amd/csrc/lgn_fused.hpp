@@ -177,7 +177,8 @@ void lgn_fused_kernel(
     };
     auto finish = [&](int ts, const float *rstd, const float *nmr) {
         if constexpr (STAGED) {
-            typedef BlockStore<Cfg::WC> BS_;
+            // the final output is streamed; u of the wide mode is re-read by the second kernel
+            typedef BlockStore<Cfg::WC, !WIDE> BS_;
             BS_::store(smem + wave * BS_::BYTES, lane,
                        [&](int tc, int q) { return normalise(ts, tc, q, rstd, nmr); }, out, N, M,
                        m0 + ws0 + 32 * ts, n0 + wc0);
