@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kSghThreads) void lgn_sgh_stats_kernel(
     if (tid == 0) part[gi * parts + p] = make_float2(mean, m2);
 }
 
-// Apply kernel: same grid; out may be y itself (each element is read and
-// then written by the same thread).  gamma/beta of the group's channels are
+// Apply kernel: same grid, walked from the last chunk to the first; out may
+// be y itself (each element is read and then written by the same thread).  gamma/beta of the group's channels are
 // folded with the statistics into per-channel (a, b) in LDS.  A thread loads
 // its float4s first (all in flight at once), then walks them with an
 // incrementally advanced channel index, keeping the coefficients of the
@@ -172,8 +172,13 @@ __global__ __launch_bounds__(kSghThreads) void lgn_sgh_apply_kernel(
     __shared__ float red[3 * (kSghThreads / 64)];
     __shared__ float coef_a[MAXCG + 1], coef_b[MAXCG + 1];
     const int tid = threadIdx.x;
-    const long long gi = g_first + blockIdx.x / parts;
-    const int p = blockIdx.x % parts;
+    // Last chunk first: the stats pass has just read the end of y, the part
+    // the MALL still holds when this pass starts.  The stores of out are
+    // non-temporal so that they do not displace it.  (At 128 x 16 x 123039
+    // fp32: 0.560 ms -> 0.549 ms reversed, 0.547 ms streamed, 0.525 ms both.)
+    const unsigned bid = gridDim.x - 1 - blockIdx.x;
+    const long long gi = g_first + bid / parts;
+    const int p = bid % parts;
     const long long n = gi / G, g = gi % G;
     const int cg = C / G;
     const long long L = (long long)cg * S;
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kSghThreads) void lgn_sgh_apply_kernel(
     };
     if (ei >= 0) {
         const int c = (int)((ei - base) / S);
-        out[ei] = act(__builtin_fmaf(swish(ev), coef_a[c], coef_b[c]));
+        __builtin_nontemporal_store(act(__builtin_fmaf(swish(ev), coef_a[c], coef_b[c])), &out[ei]);
     }
     f32x4 *obody = reinterpret_cast<f32x4 *>(out + sp.a0);
     long long r = sp.a0 - base + 4LL * tid;   // group-relative index of this thread's float4
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(kSghThreads) void lgn_sgh_apply_kernel(
                 o[j] = act(__builtin_fmaf(swish(v[k][j]), coef_a[ci], coef_b[ci]));
             }
         }
-        if (f < nb4) obody[f] = o;
+        if (f < nb4) __builtin_nontemporal_store(o, &obody[f]);
         off += 4 * kSghThreads;
         if (off >= S) {
             while (off >= S) {
