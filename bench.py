@@ -456,7 +456,7 @@ def main():
     ap.add_argument("--fused-phases", action="store_true",
                     help="instead of the forward, run the fused-tile phase probe (shader cycles "
                          "of the main loop, epilogue and store drain per tile, and the clock) at "
-                         "the pages' shape in bf16 and fp32, and exit")
+                         "the pages' shape in bf16, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the forward, run 5 plain device copies of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters) and exit")
