@@ -2,7 +2,8 @@
 """Benchmark of the fused Linear -> Swish -> +bias -> GroupNorm forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--variant fused|twopass] [--no-cpu-baseline] [--no-extra]
+                    [--variant fused|twopass|wide|lse|sgh|lnconv]
+                    [--no-cpu-baseline] [--no-extra]
 
 A step is one full forward (GEMM, bias, Swish, bias, GroupNorm statistics,
 normalise, affine, output write) over one batch of seeded synthetic input that
@@ -11,14 +12,20 @@ bracketed by torch.cuda.synchronize().  Prints ONE JSON line on stdout; a
 human-readable summary goes to stderr.
 
 value      : GEMM TFLOP/s of the whole timed region, 2*M*N*K*K_steps / wall time.
-roofline   : the fused kernel's mean time per launch from one HIP event pair
-             recorded on the launch stream around the timed launches, against the MI355X
+roofline   : the kernel's mean time per launch from one HIP event pair recorded
+             on the launch stream around the timed launches, against the MI355X
              dense MFMA peak of its input type (fp32 157.3, bf16 2500 TFLOP/s).
              traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
              counters (profiles/traffic.json), only if the kernel sources are
              unchanged since the counters were taken, else null.
-cpu_baseline: the fp64 CPU oracle timed on the host on the first S rows of the
-             same workload (S sized to about --cpu-seconds of work).
+extra      : the other workloads and entry points, timed the same way.
+telemetry  : the GPU's shader clock and board power sampled from sysfs during
+             the timed regions, and the host CPU model.
+cpu_baseline: the fp64 CPU oracle, built for this host, timed on the first S
+             rows of the workload (S sized to about --cpu-seconds of work).
+             The same leg computes the oracle over EVERY element of every
+             timed output and reports, per line, max abs, mean abs and the
+             count above the tolerance ("check").
 """
 from __future__ import annotations
 
@@ -26,7 +33,10 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import tempfile
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused Linear+Swish+bias+GroupNorm TFLOP/s at M32768 K1024 N4096; % MFMA peak"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 HBM_PEAK_GBPS = 8000.0
+TOL = {"f32": 2e-4, "bf16": 3e-2}
 DEFAULT_WORKLOAD = "m32768_k1024_n4096_g64_f32"
 
 
@@ -45,11 +56,9 @@ def eprint(*a):
 # Sources each variant's kernels are built from (a change to any of them
 # voids that variant's stored counter values).
 KERNEL_SOURCES = {
-    "fused": ("lgn_device.hpp", "lgn_fused.hpp", "lgn_fused_impl.hpp", "lgn_fused_f32.hip",
-              "lgn_fused_bf16.hip"),
+    "fused": ("lgn_device.hpp", "lgn_fused.hpp", "lgn_fused.hip"),
     "twopass": ("lgn_device.hpp", "lgn_twopass.hpp", "lgn_twopass.hip"),
-    "wide": ("lgn_device.hpp", "lgn_fused.hpp", "lgn_wide.hpp", "lgn_wide_impl.hpp",
-             "lgn_wide_f32.hip", "lgn_wide_bf16.hip"),
+    "wide": ("lgn_device.hpp", "lgn_fused.hpp", "lgn_wide.hpp", "lgn_wide.hip"),
     "lse": ("lgn_device.hpp", "lgn_lse.hpp", "lgn_lse.hip"),
     "lnconv": ("lgn_device.hpp", "lgn_sgh.hpp", "lgn_lnconv.hpp", "lgn_lnconv.hip"),
     "sgh": ("lgn_device.hpp", "lgn_sgh.hpp", "lgn_sgh.hip"),
@@ -81,6 +90,127 @@ def traffic_for(workload: str, variant: str):
     return rec.get("traffic_bytes")
 
 
+def sha256s(arrays: dict) -> dict:
+    """SHA-256 of each input array's bytes (the exact values both sides see)."""
+    import numpy as np
+    return {k: hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()
+            for k, v in sorted(arrays.items())}
+
+
+# ------------------------------------------------------------ telemetry ----
+
+def host_info() -> dict:
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:   # lscpu missing: fall back to /proc/cpuinfo
+        pass
+    if model is None:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+class Telemetry:
+    """Samples the GPU's shader clock (amdgpu hwmon freq1_input labelled
+    "sclk") and board power (hwmon power1_average or power1_input) from sysfs
+    every `interval` seconds in a background thread, and summarises the
+    samples that fall inside each named window (the timed regions)."""
+
+    def __init__(self, interval: float = 0.02):
+        self.interval = interval
+        self.samples = []          # (t, sclk_mhz or None, power_w or None)
+        self.windows = {}          # name -> (t0, t1)
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._sclk, self._power = self._find()
+
+    def _find(self):
+        try:
+            import torch
+            p = torch.cuda.get_device_properties(0)
+            pci = "%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+        except Exception as e:   # no device properties: nothing to sample
+            self.source = "unavailable (%s)" % e
+            return None, None
+        hw = os.path.join("/sys/bus/pci/devices", pci, "hwmon")
+        sclk = power = None
+        if os.path.isdir(hw):
+            for d in sorted(os.listdir(hw)):
+                dd = os.path.join(hw, d)
+                try:
+                    with open(os.path.join(dd, "freq1_label")) as f:
+                        if f.read().strip() == "sclk":
+                            sclk = os.path.join(dd, "freq1_input")
+                except OSError:
+                    pass
+                for f in ("power1_average", "power1_input"):
+                    if power is None and os.path.exists(os.path.join(dd, f)):
+                        power = os.path.join(dd, f)
+        self.source = {"pci": pci, "sclk": sclk, "power": power}
+        return sclk, power
+
+    @staticmethod
+    def _read(path, scale):
+        if path is None:
+            return None
+        try:
+            with open(path) as f:
+                return int(f.read().strip()) * scale
+        except (OSError, ValueError):
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            self.samples.append((time.perf_counter(), self._read(self._sclk, 1e-6),
+                                 self._read(self._power, 1e-6)))
+            self._stop.wait(self.interval)
+
+    def start(self):
+        if self._sclk or self._power:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def window(self, name, t0, t1):
+        self.windows[name] = (t0, t1)
+
+    def summary(self, name):
+        if name not in self.windows:
+            return None
+        t0, t1 = self.windows[name]
+        sel = [s for s in self.samples if t0 <= s[0] <= t1]
+        out = {"samples": len(sel)}
+        for i, key in ((1, "sclk_mhz"), (2, "power_w")):
+            v = sorted(s[i] for s in sel if s[i] is not None)
+            if v:
+                out[key] = {"min": round(v[0], 1), "median": round(v[len(v) // 2], 1),
+                            "max": round(v[-1], 1)}
+        return out
+
+
+# --------------------------------------------------------------- timing ----
+
 class _Timed:
     """time(): W warm-up launches, then K timed ones on self.stream."""
 
@@ -89,7 +219,7 @@ class _Timed:
         duration from one HIP event pair on the launch stream around them.
         `warmup` untimed launches first; with min_warm_ms > 0 the warm-up goes
         on until that much GPU time has passed (the clocks ramp up under load
-        over tens of milliseconds)."""
+        over tens of milliseconds).  Returns (wall, mean_ms, t0, t1)."""
         import torch
         t_warm = time.perf_counter()
         for _ in range(warmup):
@@ -107,19 +237,19 @@ class _Timed:
             self.launch()
         end.record(self.stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return wall, start.elapsed_time(end) / steps
+        t1 = time.perf_counter()
+        return t1 - t0, start.elapsed_time(end) / steps, t0, t1
 
     def distribution(self, launches: int = 50, flush_bytes: int = 0):
         """Per-launch durations (one HIP event pair around each launch on the
         launch stream): median, p10 and p90 in ms.  With flush_bytes > 0 a
         buffer of that size is overwritten between launches (outside the event
-        pair), so that x and W no longer sit in L2 or MALL when a launch starts."""
+        pair), so that the inputs no longer sit in L2 or MALL when a launch starts."""
         import numpy as np
         import torch
         buf = None
         if flush_bytes:
-            buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device=self.out.device)
+            buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(launches)]
         with torch.cuda.stream(self.stream):
@@ -144,104 +274,84 @@ class _Timed:
                 "flushed_p10_ms": cold["p10_ms"], "flushed_p90_ms": cold["p90_ms"],
                 "flush_bytes": 1 << 30}
 
+    def host_output(self):
+        """The output of the last launch, copied to host memory."""
+        import torch
+        torch.cuda.synchronize()
+        return self.out.cpu().numpy()
+
+
+def gemm_device_inputs(w, inp):
+    import numpy as np
+    import torch
+    dev = "cuda:0"
+    d = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+         for k in ("b_lin", "b_add", "gamma", "beta")}
+    for k in ("x", "W"):
+        if w.dtype == "bf16":
+            d[k] = torch.from_numpy(inp[k + "_bf16"].view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            d[k] = torch.from_numpy(inp[k]).to(dev)
+    return d
+
 
 class Runner(_Timed):
-    """Inputs resident on the GPU plus a launch() closure for one forward."""
+    """One entry point (fused, twopass, wide, lse) on a GEMM workload whose
+    inputs are resident on the GPU; launch() is one forward."""
 
-    def __init__(self, w, variant: str):
-        import numpy as np
+    def __init__(self, w, variant: str, d):
         import torch
         from gemm_activation_groupnorm_amd import lgn
-        from gemm_activation_groupnorm_amd.inputs import workload_inputs
 
         self.w, self.variant = w, variant
-        t0 = time.perf_counter()
-        self.inp = workload_inputs(w)
         dev = "cuda:0"
-        self.d = {k: torch.from_numpy(np.ascontiguousarray(self.inp[k])).to(dev)
-                  for k in ("b_lin", "b_add", "gamma", "beta")}
-        if w.dtype == "bf16":
-            for k in ("x", "W"):
-                self.d[k] = torch.from_numpy(self.inp[k + "_bf16"].view(np.int16)).to(dev).view(
-                    torch.bfloat16)
-        else:
-            for k in ("x", "W"):
-                self.d[k] = torch.from_numpy(self.inp[k]).to(dev)
         self.ws = None
         if variant == "lse":
             self.out = torch.empty(w.M, dtype=torch.float32, device=dev)
-            nb_lse = lgn.lgn_lse_workspace_bytes(w.M, w.N)
-            self.ws = torch.empty(max(1, nb_lse // 4), dtype=torch.float32, device=dev)
+            nb = lgn.lgn_lse_workspace_bytes(w.M, w.N)
         else:
             self.out = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
-        if variant == "twopass":
-            self.ws = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
-        if variant == "wide":
-            nb_wide = lgn.lgn_wide_workspace_bytes(w.M, w.N)
-            self.ws = torch.empty(max(1, nb_wide // 4), dtype=torch.float32, device=dev)
-        torch.cuda.synchronize()
-        eprint("[bench] %s/%s inputs ready in %.1f s" % (w.name, variant, time.perf_counter() - t0))
+            nb = {"twopass": lgn.lgn_twopass_workspace_bytes(w.M, w.N),
+                  "wide": lgn.lgn_wide_workspace_bytes(w.M, w.N)}.get(variant, 0)
+        if nb:
+            self.ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device=dev)
         self.stream = torch.cuda.current_stream()
-        d, out = self.d, self.out
+        out, ws, s = self.out, self.ws, self.stream
         args = (d["x"], d["W"], d["b_lin"], d["b_add"], d["gamma"], d["beta"],
                 w.M, w.K, w.N, w.G, w.eps, out)
-        s = self.stream
+        f32 = w.dtype == "f32"
         if variant == "fused":
-            fn = lgn.lgn_forward_f32 if w.dtype == "f32" else lgn.lgn_forward_bf16
+            fn = lgn.lgn_forward_f32 if f32 else lgn.lgn_forward_bf16
             self.launch = lambda: lgn.check(fn(*args, stream=s))
-        elif variant == "wide":
-            fn = lgn.lgn_forward_wide_f32 if w.dtype == "f32" else lgn.lgn_forward_wide_bf16
-            ws, nb_wide = self.ws, lgn.lgn_wide_workspace_bytes(w.M, w.N)
-            self.launch = lambda: lgn.check(fn(*args, ws, nb_wide, stream=s))
         elif variant == "lse":
-            fn = lgn.lgn_linear_lse_f32 if w.dtype == "f32" else lgn.lgn_linear_lse_bf16
-            ws, nb_lse = self.ws, lgn.lgn_lse_workspace_bytes(w.M, w.N)
-            lse_args = (d["x"], d["W"], d["b_lin"], w.M, w.K, w.N, out, ws, nb_lse)
-            self.launch = lambda: lgn.check(fn(*lse_args, stream=s))
+            fn = lgn.lgn_linear_lse_f32 if f32 else lgn.lgn_linear_lse_bf16
+            largs = (d["x"], d["W"], d["b_lin"], w.M, w.K, w.N, out, ws, nb)
+            self.launch = lambda: lgn.check(fn(*largs, stream=s))
         else:
-            fn = lgn.lgn_forward_twopass_f32 if w.dtype == "f32" else lgn.lgn_forward_twopass_bf16
-            nb = lgn.lgn_twopass_workspace_bytes(w.M, w.N)
-            ws = self.ws
+            fn = {("twopass", True): lgn.lgn_forward_twopass_f32,
+                  ("twopass", False): lgn.lgn_forward_twopass_bf16,
+                  ("wide", True): lgn.lgn_forward_wide_f32,
+                  ("wide", False): lgn.lgn_forward_wide_bf16}[(variant, f32)]
             self.launch = lambda: lgn.check(fn(*args, ws, nb, stream=s))
 
-    def check_rows(self, nrows: int = 8):
-        import numpy as np
-        import oracle
-        from gemm_activation_groupnorm_amd.inputs import sample_rows
-        rows = sample_rows(self.w.M, nrows, seed=99)
-        import torch
-        idx = torch.from_numpy(rows).to(self.out.device)
-        y = self.out[idx].cpu().numpy().astype(np.float64)
-        i = self.inp
-        if self.variant == "lse":
-            ref = oracle.linear_lse_forward(i["x"][rows], i["W"], i["b_lin"])
-        else:
-            ref = oracle.lgn_forward(i["x"][rows], i["W"], i["b_lin"], i["b_add"], i["gamma"],
-                                     i["beta"], self.w.G, self.w.eps)
-        return float(np.max(np.abs(y - ref))), len(rows)
+    @property
+    def flops(self) -> int:
+        return self.w.flops
 
 
 class SghRunner(_Timed):
     """Swish -> spatial GroupNorm -> HardSwish on y [Nb, C, D*H*W], resident."""
 
-    def __init__(self, w):
-        import numpy as np
+    def __init__(self, w, d):
         import torch
         from gemm_activation_groupnorm_amd import lgn
-        from gemm_activation_groupnorm_amd.inputs import make_sgh_inputs
 
         self.w, self.variant = w, "sgh"
-        t0 = time.perf_counter()
-        self.inp = make_sgh_inputs(w.Nb, w.C, w.S, w.seed)
-        self.d = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda:0")
-                  for k, v in self.inp.items()}
-        self.out = torch.empty_like(self.d["y"])
+        self.out = torch.empty_like(d["y"])
         nb = lgn.lgn_sgh_workspace_bytes(w.Nb, w.C, w.S, w.G)
         self.ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device="cuda:0")
-        torch.cuda.synchronize()
-        eprint("[bench] %s/sgh inputs ready in %.1f s" % (w.name, time.perf_counter() - t0))
         self.stream = torch.cuda.current_stream()
-        d, s = self.d, self.stream
+        s = self.stream
         args = (d["y"], d["gamma"], d["beta"], w.Nb, w.C, w.S, w.G, w.eps, self.out, self.ws, nb)
         self.launch = lambda: lgn.check(lgn.lgn_swish_gn_hardswish_f32(*args, stream=s))
 
@@ -250,88 +360,208 @@ class SghRunner(_Timed):
         """One read of y and one write of out (gamma, beta are 2*C floats)."""
         return 2 * self.w.elements * 4 + 2 * self.w.C * 4
 
-    def check_rows(self, nrows: int = 2):
-        """Max abs error against the oracle on `nrows` whole samples."""
-        import numpy as np
-        import oracle
-        import torch
-        from gemm_activation_groupnorm_amd.inputs import sample_rows
-        rows = sample_rows(self.w.Nb, nrows, seed=99)
-        y = self.out[torch.from_numpy(rows).to(self.out.device)].cpu().numpy().astype(np.float64)
-        ref = oracle.swish_gn_hardswish(self.inp["y"][rows], self.inp["gamma"], self.inp["beta"],
-                                        self.w.G, self.w.eps)
-        return float(np.max(np.abs(y - ref))), len(rows)
-
 
 class LnConvRunner(_Timed):
     """LayerNorm -> GELU -> dilated Conv1d -> + input on x [B, C, L], resident."""
 
-    def __init__(self, w):
-        import numpy as np
+    def __init__(self, w, d):
         import torch
         from gemm_activation_groupnorm_amd import lgn
-        from gemm_activation_groupnorm_amd.inputs import make_lnconv_inputs
 
         self.w, self.variant = w, "lnconv"
-        t0 = time.perf_counter()
-        self.inp = make_lnconv_inputs(w.B, w.C, w.L, w.seed)
-        self.d = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda:0")
-                  for k, v in self.inp.items()}
-        self.out = torch.empty_like(self.d["x"])
+        self.out = torch.empty_like(d["x"])
         nb = lgn.lgn_lnconv_workspace_bytes(w.B, w.C, w.L)
         self.ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device="cuda:0")
-        torch.cuda.synchronize()
-        eprint("[bench] %s/lnconv inputs ready in %.1f s" % (w.name, time.perf_counter() - t0))
         self.stream = torch.cuda.current_stream()
-        d, s = self.d, self.stream
+        s = self.stream
         args = (d["x"], d["ln_w"], d["ln_b"], d["conv_w"], d["conv_b"], w.B, w.C, w.L, w.dilation,
                 w.eps, w.gelu_tanh, self.out, self.ws, nb)
         self.launch = lambda: lgn.check(lgn.lgn_ln_gelu_conv1d_f32(*args, stream=s))
 
-    def check_rows(self, ncols: int = 16):
-        """Max abs error against the oracle on `ncols` sampled output columns (b, :, j)."""
-        import numpy as np
-        import oracle
-        r = np.random.default_rng(99)
+    @property
+    def flops(self) -> int:
+        return self.w.flops
+
+
+# ------------------------------------------------------------ workloads ----
+
+class Workload:
+    """A workload's seeded inputs (host and device) and its timed entry points."""
+
+    def __init__(self, name: str):
+        from gemm_activation_groupnorm_amd import inputs as I
+        self.name = name
+        t0 = time.perf_counter()
+        for lst, kind in ((I.WORKLOADS + I.WIDE_WORKLOADS + I.LSE_WORKLOADS, "gemm"),
+                          (I.SGH_WORKLOADS, "sgh"), (I.LNCONV_WORKLOADS, "lnconv")):
+            m = [x for x in lst if x.name == name]
+            if m:
+                self.w, self.kind = m[0], kind
+                break
+        else:
+            raise SystemExit("unknown workload %r" % name)
         w = self.w
-        cols = [(int(b), int(j)) for b, j in zip(r.integers(0, w.B, ncols), r.integers(0, w.L, ncols))]
-        ref = oracle.ln_gelu_conv1d_cols(self.inp["x"], self.inp["ln_w"], self.inp["ln_b"],
-                                         self.inp["conv_w"], self.inp["conv_b"], w.dilation, w.eps,
-                                         cols, gelu_tanh=w.gelu_tanh)
-        y = np.stack([self.out[b, :, j].cpu().numpy() for b, j in cols]).astype(np.float64)
-        return float(np.max(np.abs(y - ref))), len(cols)
+        if self.kind == "gemm":
+            self.inp = I.workload_inputs(w)
+            self.d = gemm_device_inputs(w, self.inp)
+            self.dtype = w.dtype
+        else:
+            import numpy as np
+            import torch
+            self.inp = (I.make_sgh_inputs(w.Nb, w.C, w.S, w.seed) if self.kind == "sgh" else
+                        I.make_lnconv_inputs(w.B, w.C, w.L, w.seed))
+            self.d = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda:0")
+                      for k, v in self.inp.items()}
+            self.dtype = "f32"
+        # hash what the GPU reads (bf16 workloads: the bf16 bits of x and W)
+        if self.kind == "gemm" and w.dtype == "bf16":
+            hashed = {k: v for k, v in self.inp.items() if k not in ("x", "W")}
+        else:
+            hashed = self.inp
+        self.sha256 = sha256s(hashed)
+        eprint("[bench] %s inputs ready in %.1f s" % (name, time.perf_counter() - t0))
+
+    def runner(self, variant: str):
+        if self.kind == "sgh":
+            return SghRunner(self.w, self.d)
+        if self.kind == "lnconv":
+            return LnConvRunner(self.w, self.d)
+        return Runner(self.w, variant, self.d)
+
+    def release(self):
+        import torch
+        self.d = None
+        torch.cuda.empty_cache()
 
 
-def lnconv_main(args):
-    """One JSON line for the LayerNorm -> GELU -> dilated Conv1d -> + input path
-    (three launches per step), as convolution TFLOP/s."""
-    from gemm_activation_groupnorm_amd.inputs import LNCONV_WORKLOADS
-    w = [x for x in LNCONV_WORKLOADS if x.name == args.workload]
-    if not w:
-        raise SystemExit("--variant lnconv needs one of: %s" % [x.name for x in LNCONV_WORKLOADS])
-    w = w[0]
-    r = LnConvRunner(w)
-    wall, kmean = r.time(args.steps, args.warmup)
-    ach = w.flops / (kmean * 1e-3) / 1e12
-    err, ncols = r.check_rows()
-    eprint("[bench] %s/lnconv: %.3f ms/step, kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f); "
-           "sampled-column max err %.2e" % (w.name, wall / args.steps * 1e3, kmean, ach,
-                                            100 * ach / PEAK_TFLOPS["f32"], PEAK_TFLOPS["f32"], err))
-    print(json.dumps({
-        "metric": "LayerNorm->GELU->dilated Conv1d->+x convolution TFLOP/s", "value": round(
-            w.flops / (wall / args.steps) / 1e12, 3),
-        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "C": w.C, "L": w.L, "dilation": w.dilation,
-                   "eps": w.eps, "gelu": "tanh" if w.gelu_tanh else "exact", "seed": w.seed,
-                   "variant": "lnconv"},
-        "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_TFLOPS["f32"],
-                     "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS["f32"], 4),
-                     "traffic": traffic_for(w.name, "lnconv"), "kernel_ms_mean": round(kmean, 4),
-                     "kernel": "wpack+stats+lnconv"},
-        "check": {"columns": ncols, "max_abs_err_vs_oracle": err}}), flush=True)
+def measure(wl: Workload, variant: str, steps: int, warmup: int, tel: Telemetry,
+            min_warm_ms: float = 0.0, per_launch: bool = False) -> dict:
+    """Times one entry point on one workload; returns its record (with the
+    output kept on the host for the oracle leg under "_host")."""
+    r = wl.runner(variant)
+    wall, kmean, t0, t1 = r.time(steps, warmup, min_warm_ms)
+    key = "%s/%s" % (wl.name, variant)
+    tel.window(key, t0, t1)
+    rec = {"workload": wl.name, "variant": variant, "dtype": wl.dtype,
+           "ms_per_step": round(wall / steps * 1e3, 4), "kernel_ms_mean": round(kmean, 4),
+           "_wall": wall, "_kmean": kmean}
+    if wl.kind == "sgh":
+        gbps = r.algorithmic_bytes / (kmean * 1e-3) / 1e9
+        rec.update(algorithmic_gbps=round(gbps, 1), frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
+        msg = "%.0f GB/s algorithmic (%.1f%% of %.0f)" % (gbps, 100 * gbps / HBM_PEAK_GBPS,
+                                                          HBM_PEAK_GBPS)
+    else:
+        ach = r.flops / (kmean * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[wl.dtype]
+        rec.update(tflops=round(ach, 3), frac_of_peak=round(ach / peak, 4))
+        msg = "%.1f TFLOP/s (%.1f%% of %.1f)" % (ach, 100 * ach / peak, peak)
+    if per_launch:
+        rec["per_launch"] = r.distributions()
+    rec["telemetry"] = tel.summary(key)
+    rec["_host"] = r.host_output()
+    eprint("[bench] %s: %.3f ms/step, kernel mean %.4f ms -> %s" % (key, wall / steps * 1e3,
+                                                                    kmean, msg))
+    del r
+    return rec
 
+
+# --------------------------------------------------- cpu_baseline leg ----
+# Everything below touches the oracle: its timing on the host, and the
+# comparison of every timed output with its fp64 results.
+
+class ErrStats:
+    """max abs, mean abs and count above the tolerance over compared elements."""
+
+    def __init__(self, tol: float):
+        self.tol, self.max, self.sum, self.n, self.over, self.nonfinite = tol, 0.0, 0.0, 0, 0, 0
+
+    def add(self, y, ref):
+        import numpy as np
+        fin = np.isfinite(y)
+        self.nonfinite += int(y.size - np.count_nonzero(fin))
+        d = np.abs(y.astype(np.float64) - ref)
+        d[~fin] = np.inf
+        if d.size:
+            self.max = max(self.max, float(d.max()))
+            self.sum += float(d[fin].sum())
+        self.n += d.size
+        self.over += int(np.count_nonzero(d > self.tol))
+
+    def summary(self) -> dict:
+        return {"elements": self.n, "max_abs_err": self.max,
+                "mean_abs_err": self.sum / self.n if self.n else 0.0,
+                "count_gt_tol": self.over, "nonfinite": self.nonfinite, "tol": self.tol,
+                "vs": "fp64 oracle, every element"}
+
+
+def check_outputs(wl: Workload, recs: list) -> None:
+    """Compares every element of each record's output with the oracle (one
+    oracle pass per chunk of rows, shared by the workload's records)."""
+    import oracle
+    t0 = time.perf_counter()
+    w, i = wl.w, wl.inp
+    if wl.kind == "sgh":
+        rows, chunk = w.Nb, 16
+        ref_of = lambda a, b: oracle.swish_gn_hardswish(i["y"][a:b], i["gamma"], i["beta"], w.G,
+                                                        w.eps)
+    elif wl.kind == "lnconv":
+        rows, chunk = w.B, 16
+        ref_of = lambda a, b: oracle.ln_gelu_conv1d(i["x"][a:b], i["ln_w"], i["ln_b"],
+                                                    i["conv_w"], i["conv_b"], w.dilation, w.eps,
+                                                    gelu_tanh=w.gelu_tanh)
+    elif all(r["variant"] == "lse" for r in recs):
+        rows, chunk = w.M, 256
+        ref_of = lambda a, b: oracle.linear_lse_forward(i["x"][a:b], i["W"], i["b_lin"])
+    else:
+        assert not any(r["variant"] == "lse" for r in recs)
+        rows, chunk = w.M, 2048
+        ref_of = lambda a, b: oracle.lgn_forward(i["x"][a:b], i["W"], i["b_lin"], i["b_add"],
+                                                 i["gamma"], i["beta"], w.G, w.eps)
+    stats = [ErrStats(TOL[wl.dtype]) for _ in recs]
+    for a in range(0, rows, chunk):
+        b = min(rows, a + chunk)
+        ref = ref_of(a, b)
+        for st, r in zip(stats, recs):
+            st.add(r["_host"][a:b], ref)
+    for st, r in zip(stats, recs):
+        r["check"] = st.summary()
+        eprint("[bench] check %s/%s: max abs %.3e, mean abs %.3e, %d of %d > %.0e (%.1f s)"
+               % (wl.name, r["variant"], st.max, r["check"]["mean_abs_err"], st.over, st.n,
+                  st.tol, time.perf_counter() - t0))
+
+
+def cpu_baseline(wl: Workload, seconds: float, tmpdir: str) -> dict:
+    """The oracle, compiled with -O3 -march=native on this host, timed on the
+    first rows of the workload (about `seconds` of work; OpenMP over rows on
+    every host thread), as GEMM TFLOP/s of its fp64 arithmetic."""
+    import oracle
+    path = oracle.use_native_build(tmpdir)
+    w, i = wl.w, wl.inp
+    args = (i["b_lin"], i["b_add"], i["gamma"], i["beta"], w.G, w.eps)
+    probe = min(w.M, 64)
+    t0 = time.perf_counter()
+    oracle.lgn_forward(i["x"][:probe], i["W"], *args)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(max(probe, min(w.M, seconds / max(per_row, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.lgn_forward(i["x"][:rows], i["W"], *args)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    hi = host_info()
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "first %d of %d rows of %s, fp64 C oracle built with %s, %.1f s wall, %d "
+                  "OpenMP threads on %s" % (rows, w.M, w.name, " ".join(oracle.NATIVE_CFLAGS[:2]),
+                                            dt, oracle.num_threads(), hi["cpu_model"]),
+        "cpu_model": hi["cpu_model"],
+        "build": os.path.basename(path),
+    }
+
+
+# ----------------------------------------------------------------- main ----
 
 def torch_context(w):
     """Context only: torch's linear (vendor GEMM, output in the input type) and
@@ -369,57 +599,59 @@ def torch_context(w):
             "note": "context only: torch linear = vendor GEMM with output in the input type"}
 
 
-def cpu_baseline(w, inp, seconds: float):
-    import oracle
-    x, W = inp["x"], inp["W"]
-    args = (inp["b_lin"], inp["b_add"], inp["gamma"], inp["beta"], w.G, w.eps)
-    probe = min(w.M, 32)
-    t0 = time.perf_counter()
-    oracle.lgn_forward(x[:probe], W, *args)
-    per_row = (time.perf_counter() - t0) / probe
-    rows = int(max(probe, min(w.M, seconds / max(per_row, 1e-9))))
-    t0 = time.perf_counter()
-    oracle.lgn_forward(x[:rows], W, *args)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * w.N * w.K
-    return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
-        "cores": oracle.num_threads(),
-        "kind": "oracle",
-        "sample": "first %d of %d rows of %s, fp64 C oracle, %.1f s wall, %d OpenMP threads"
-                  % (rows, w.M, w.name, dt, oracle.num_threads()),
-    }
+# The secondary lines, grouped by workload so that each oracle pass serves
+# every entry point timed on it.
+EXTRA = [
+    (DEFAULT_WORKLOAD, ["fused", "twopass"]),
+    ("m32768_k1024_n4096_g64_bf16", ["fused", "twopass"]),
+    ("m16384_k2048_n8192_g8_f32", ["fused", "twopass", "wide"]),
+    ("m16384_k2048_n8192_g1_f32", ["wide"]),
+    ("m1024_k8192_n8192_lse_f32", ["lse"]),
+    ("m1024_k8192_n8192_lse_bf16", ["lse"]),
+    ("n128_c16_d31_h63_w63_g4_sgh_f32", ["sgh"]),
+    ("b32_c256_l4096_d4_lnconv_f32", ["lnconv"]),
+]
 
 
-def sgh_main(args):
-    """One JSON line for the HBM-bound Swish -> spatial GroupNorm -> HardSwish
-    kernels (two launches per step), as GB/s of algorithmic traffic."""
-    from gemm_activation_groupnorm_amd.inputs import SGH_WORKLOADS
-    w = [x for x in SGH_WORKLOADS if x.name == args.workload]
-    if not w:
-        raise SystemExit("--variant sgh needs one of: %s" % [x.name for x in SGH_WORKLOADS])
-    w = w[0]
-    r = SghRunner(w)
-    wall, kmean = r.time(args.steps, args.warmup)
-    gbps = r.algorithmic_bytes / (kmean * 1e-3) / 1e9
-    err, nrows = r.check_rows()
-    eprint("[bench] %s/sgh: %.3f ms/step, kernel mean %.3f ms -> %.0f GB/s algorithmic (%.1f%% of "
-           "%.0f); sampled-sample max err %.2e"
-           % (w.name, wall / args.steps * 1e3, kmean, gbps, 100 * gbps / HBM_PEAK_GBPS,
-              HBM_PEAK_GBPS, err))
-    print(json.dumps({
-        "metric": "Swish->spatial GroupNorm->HardSwish algorithmic HBM GB/s", "value": round(gbps, 1),
-        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.name, "Nb": w.Nb, "C": w.C, "D": w.D, "H": w.H, "W": w.W,
-                   "G": w.G, "eps": w.eps, "seed": w.seed, "variant": "sgh"},
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_for(w.name, "sgh"), "kernel_ms_mean": round(kmean, 4),
-                     "kernel": "sgh stats+apply"},
-        "check": {"samples": nrows, "max_abs_err_vs_oracle": err}}), flush=True)
+def headline_json(wl: Workload, rec: dict, args) -> dict:
+    w = wl.w
+    wall, kmean = rec["_wall"], rec["_kmean"]
+    ms = wall / args.steps * 1e3
+    base = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": wl.dtype, "data": "synthetic"}
+    cfg = {"workload": w.name, "variant": rec["variant"], "seed": w.seed, "eps": w.eps,
+           "inputs_sha256": wl.sha256}
+    if wl.kind == "sgh":
+        gbps = rec["algorithmic_gbps"]
+        cfg.update(Nb=w.Nb, C=w.C, D=w.D, H=w.H, W=w.W, G=w.G)
+        return {"metric": "Swish->spatial GroupNorm->HardSwish algorithmic HBM GB/s",
+                "value": round((2 * w.elements * 4 + 2 * w.C * 4) / (ms * 1e-3) / 1e9, 1),
+                "unit": "GB/s", **base, "config": cfg,
+                "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                             "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                             "traffic": traffic_for(w.name, "sgh"),
+                             "kernel_ms_mean": round(kmean, 4), "kernel": "sgh stats+apply"}}
+    ach = w.flops / (kmean * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    if wl.kind == "lnconv":
+        cfg.update(B=w.B, C=w.C, L=w.L, dilation=w.dilation,
+                   gelu="tanh" if w.gelu_tanh else "exact")
+        metric = "LayerNorm->GELU->dilated Conv1d->+x convolution TFLOP/s"
+        kernel = "wpack+stats+lnconv"
+    else:
+        cfg.update(M=w.M, K=w.K, N=w.N, G=w.G,
+                   inputs="x~%g*N(0,1); W,b_lin~U(+-1/sqrt(K)); b_add~0.02*N(0,1); "
+                          "gamma~1+0.1*N(0,1); beta~0.1*N(0,1)" % w.x_scale)
+        metric = METRIC
+        kernel = {"fused": "lgn_fused_kernel", "twopass": "gemm+epilogue",
+                  "wide": "wide partial+norm", "lse": "lse partial+finish"}[rec["variant"]]
+    return {"metric": metric, "value": round(w.flops / (ms * 1e-3) / 1e12, 3),
+            "unit": "TFLOP/s", **base, "config": cfg,
+            "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                         "traffic": traffic_for(w.name, rec["variant"]),
+                         "kernel_ms_mean": round(kmean, 4), "kernel": kernel}}
 
 
 def main():
@@ -432,10 +664,12 @@ def main():
                     choices=["fused", "twopass", "wide", "lse", "sgh", "lnconv"],
                     help="lse: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 (use with an "
                          "m1024_k8192_n8192_lse_* workload); sgh: Swish -> spatial GroupNorm -> "
-                         "HardSwish (use with an *_sgh_* workload; reports GB/s)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+                         "HardSwish (reports GB/s); lnconv: LayerNorm -> GELU -> dilated "
+                         "Conv1d -> + x (these two pick their own workload by default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg: no CPU baseline and no per-line check")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the secondary workloads (bf16, wide group, two-pass)")
+                    help="skip the secondary workloads and entry points")
     ap.add_argument("--no-per-launch", action="store_true",
                     help="skip the per-launch (median/p10/p90, flushed) timings, e.g. under a "
                          "profiler whose kernel averages should cover the timed launches only")
@@ -443,20 +677,6 @@ def main():
     ap.add_argument("--torch-context", action="store_true",
                     help="also time, for context only, torch's linear (vendor GEMM) and the "
                          "unfused torch pipeline on the same workload")
-    ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="instead of the forward, run the MFMA-ceiling probe (sustained MFMA rate "
-                         "and shader clock for zero and random operands) and exit")
-    ap.add_argument("--lds-bandwidth", action="store_true",
-                    help="instead of the forward, run the LDS-bandwidth probe (16-byte LDS reads, "
-                         "bytes per shader clock per CU) and exit")
-    ap.add_argument("--l2-feed", action="store_true",
-                    help="instead of the forward, run the operand-feed probe (global -> LDS DMA "
-                         "of a 512-row panel with 64- or 128-byte LDS rows, bytes per shader "
-                         "clock per CU) and exit")
-    ap.add_argument("--fused-phases", action="store_true",
-                    help="instead of the forward, run the fused-tile phase probe (shader cycles "
-                         "of the main loop, epilogue and store drain per tile, and the clock) at "
-                         "the pages' shape in bf16, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the forward, run 5 plain device copies of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -469,17 +689,6 @@ def main():
               "the rows and is not run here (--gpus %d, WORLD_SIZE %d)." % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
-
-    if args.mfma_ceiling or args.lds_bandwidth or args.l2_feed or args.fused_phases:
-        # a child process of its own: this process has not touched the GPU
-        import subprocess
-        from gemm_activation_groupnorm_amd import build as hip_build
-        exe = (hip_build.PROBE if args.mfma_ceiling else
-               hip_build.LDS_PROBE if args.lds_bandwidth else
-               hip_build.FEED_PROBE if args.l2_feed else hip_build.PHASES_PROBE)
-        if not os.path.exists(exe):
-            hip_build.build_probe()
-        sys.exit(subprocess.run([exe]).returncode)
 
     import torch
     if args.copy_calibration:
@@ -495,143 +704,62 @@ def main():
     from gemm_activation_groupnorm_amd import build as hip_build
     if not os.path.exists(hip_build.LIB):
         hip_build.build()
-    from gemm_activation_groupnorm_amd.inputs import get_workload
 
-    if args.variant == "sgh":
-        sgh_main(args)
-        return
-    if args.variant == "lnconv":
-        lnconv_main(args)
-        return
-    w = get_workload(args.workload)
-    r = Runner(w, args.variant)
-    wall, kmean = r.time(args.steps, args.warmup)
-    flops = float(w.flops)
-    ms_per_step = wall / args.steps * 1e3
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kmean * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
-    dist = None if args.no_per_launch else r.distributions()
-    err, nrows = r.check_rows()
-    if dist:
-        eprint("[bench] %s/%s per launch: median %.3f ms (p10 %.3f, p90 %.3f); flushed median "
-               "%.3f ms" % (w.name, args.variant, dist["median_ms"], dist["p10_ms"], dist["p90_ms"],
-                            dist["flushed_median_ms"]))
-    eprint("[bench] %s/%s: %.3f ms/step, kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f); "
-           "sampled-row max err %.2e"
-           % (w.name, args.variant, ms_per_step, kmean, achieved, 100 * achieved / peak, peak, err))
-    res = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "G": w.G, "eps": w.eps,
-                   "seed": w.seed, "variant": args.variant,
-                   "inputs": "x~%g*N(0,1); W,b_lin~U(+-1/sqrt(K)); b_add~0.02*N(0,1); "
-                             "gamma~1+0.1*N(0,1); beta~0.1*N(0,1)" % w.x_scale},
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 3),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic_for(w.name, args.variant),
-            "kernel_ms_mean": round(kmean, 4),
-            "kernel": {"fused": "lgn_fused_kernel", "twopass": "gemm+epilogue",
-                       "wide": "wide partial+norm", "lse": "lse partial+finish"}[args.variant],
-        },
-        "per_launch": dist,
-        "check": {"rows": nrows, "max_abs_err_vs_oracle": err},
-    }
-    inp = r.inp
-    del r
-    torch.cuda.empty_cache()
-
+    tel = Telemetry().start()
+    head_name, head_var = args.workload, args.variant
+    if head_var in ("sgh", "lnconv") and args.workload == DEFAULT_WORKLOAD:
+        head_name = [n for n, v in EXTRA if head_var in v][0]
+    groups = [(head_name, [head_var])]
     if not args.no_extra:
-        extra = []
-        for name, variant in (("m32768_k1024_n4096_g64_bf16", "fused"),
-                              ("m16384_k2048_n8192_g8_f32", "fused"),
-                              (DEFAULT_WORKLOAD, "twopass"),
-                              ("m32768_k1024_n4096_g64_bf16", "twopass"),
-                              ("m16384_k2048_n8192_g8_f32", "twopass"),
-                              ("m16384_k2048_n8192_g8_f32", "wide"),
-                              ("m16384_k2048_n8192_g1_f32", "wide"),
-                              ("m1024_k8192_n8192_lse_f32", "lse"),
-                              ("m1024_k8192_n8192_lse_bf16", "lse")):
-            if name == w.name and variant == args.variant:
-                continue
-            we = get_workload(name)
-            re = Runner(we, variant)
-            n_extra = 50
-            wl, km_mean = re.time(n_extra, 5, min_warm_ms=100.0)
-            ach = we.flops / (km_mean * 1e-3) / 1e12
-            dist_e = re.distributions() if (variant == "fused" and we.dtype == "bf16") else None
-            e2, _ = re.check_rows(4)
-            eprint("[bench] %s/%s: kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f), err %.2e"
-                   % (name, variant, km_mean, ach, 100 * ach / PEAK_TFLOPS[we.dtype],
-                      PEAK_TFLOPS[we.dtype], e2))
-            extra.append({"workload": name, "variant": variant, "dtype": we.dtype,
-                          "ms_per_step": round(wl / n_extra * 1e3, 4), "kernel_ms_mean": round(km_mean, 4),
-                          "tflops": round(ach, 3), "frac_of_peak": round(ach / PEAK_TFLOPS[we.dtype], 4),
-                          "max_abs_err_vs_oracle": e2})
-            if dist_e:
-                extra[-1]["per_launch"] = dist_e
-            del re
-            torch.cuda.empty_cache()
-        from gemm_activation_groupnorm_amd.inputs import SGH_WORKLOADS
-        for ws_ in SGH_WORKLOADS:
-            if args.variant == "sgh":
-                continue
-            rs = SghRunner(ws_)
-            n_extra = 30
-            wl, km_mean = rs.time(n_extra, 3, min_warm_ms=100.0)
-            gbps = rs.algorithmic_bytes / (km_mean * 1e-3) / 1e9
-            e2, _ = rs.check_rows(2)
-            eprint("[bench] %s/sgh: kernel mean %.3f ms -> %.0f GB/s algorithmic (%.1f%% of %.0f), "
-                   "err %.2e" % (ws_.name, km_mean, gbps, 100 * gbps / HBM_PEAK_GBPS, HBM_PEAK_GBPS,
-                                 e2))
-            extra.append({"workload": ws_.name, "variant": "sgh", "dtype": "f32",
-                          "ms_per_step": round(wl / n_extra * 1e3, 4),
-                          "kernel_ms_mean": round(km_mean, 4), "algorithmic_gbps": round(gbps, 1),
-                          "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                          "max_abs_err_vs_oracle": e2})
-            del rs
-            torch.cuda.empty_cache()
-        from gemm_activation_groupnorm_amd.inputs import LNCONV_WORKLOADS
-        for wl_ in LNCONV_WORKLOADS:
-            rl = LnConvRunner(wl_)
-            n_extra = 30
-            wl, km_mean = rl.time(n_extra, 3, min_warm_ms=100.0)
-            ach = wl_.flops / (km_mean * 1e-3) / 1e12
-            e2, _ = rl.check_rows(8)
-            eprint("[bench] %s/lnconv: kernel mean %.3f ms -> %.1f TFLOP/s (%.1f%% of %.1f), "
-                   "err %.2e" % (wl_.name, km_mean, ach, 100 * ach / PEAK_TFLOPS["f32"],
-                                 PEAK_TFLOPS["f32"], e2))
-            extra.append({"workload": wl_.name, "variant": "lnconv", "dtype": "f32",
-                          "ms_per_step": round(wl / n_extra * 1e3, 4),
-                          "kernel_ms_mean": round(km_mean, 4), "tflops": round(ach, 3),
-                          "frac_of_peak": round(ach / PEAK_TFLOPS["f32"], 4),
-                          "max_abs_err_vs_oracle": e2})
-            del rl
-            torch.cuda.empty_cache()
-        res["extra"] = extra
+        for name, variants in EXTRA:
+            vs = [v for v in variants if not (name == head_name and v == head_var)]
+            if name == head_name:
+                groups[0][1].extend(vs)
+            elif vs:
+                groups.append((name, vs))
 
+    head_rec, extra, measured = None, [], []
+    for gi, (name, variants) in enumerate(groups):
+        wl = Workload(name)
+        recs = []
+        for v in variants:
+            if gi == 0 and v == head_var:
+                rec = measure(wl, v, args.steps, args.warmup, tel,
+                              per_launch=not args.no_per_launch)
+                head_rec = rec
+            else:
+                per = (not args.no_per_launch) and v == "fused" and wl.dtype == "bf16"
+                rec = measure(wl, v, 50, 5, tel, min_warm_ms=100.0, per_launch=per)
+                extra.append(rec)
+            recs.append(rec)
+        wl.release()
+        measured.append((wl, recs))
+    tel.stop()
+
+    head_wl = measured[0][0]
+    res = headline_json(head_wl, head_rec, args)
+    if head_rec.get("per_launch"):
+        res["per_launch"] = head_rec["per_launch"]
+    res["telemetry"] = {"gpu": head_rec["telemetry"], "gpu_source": tel.source,
+                        "host": host_info()}
     if args.torch_context:
-        res["torch_context"] = torch_context(w)
+        res["torch_context"] = torch_context(head_wl.w)
 
+    res["check"] = None
+    res["cpu_baseline"] = None
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
-        eprint("[bench] cpu baseline: %s" % res["cpu_baseline"]["sample"])
-    else:
-        res["cpu_baseline"] = None
+        for wl, recs in measured:
+            check_outputs(wl, recs)
+        res["check"] = head_rec["check"]
+        if head_wl.kind == "gemm" and head_rec["variant"] != "lse":
+            with tempfile.TemporaryDirectory() as td:
+                res["cpu_baseline"] = cpu_baseline(head_wl, args.cpu_seconds, td)
+            eprint("[bench] cpu baseline: %s" % res["cpu_baseline"]["sample"])
+    for r in extra:
+        for k in [k for k in r if k.startswith("_")]:
+            del r[k]
+    if extra:
+        res["extra"] = extra
     print(json.dumps(res), flush=True)
 
 

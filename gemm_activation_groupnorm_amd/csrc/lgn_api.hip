@@ -50,7 +50,15 @@ lgn_status from_hip(hipError_t e) {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
 
+bool is_gfx950(const char *arch) { return strncmp(arch, "gfx950", 6) == 0; }
+
+// Architecture name set by lgn_testing_set_arch (empty: query the device).
+char g_arch_override[64];
+std::atomic<bool> g_arch_overridden{false};
+
 lgn_status check_device() {
+    if (g_arch_overridden.load(std::memory_order_acquire))
+        return is_gfx950(g_arch_override) ? LGN_OK : LGN_ERR_UNSUPPORTED;
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return from_hip(e);
@@ -63,7 +71,7 @@ lgn_status check_device() {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return from_hip(e);
-    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    const bool ok = is_gfx950(prop.gcnArchName);
     if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
     return ok ? LGN_OK : LGN_ERR_UNSUPPORTED;
 }
@@ -306,6 +314,26 @@ const char *lgn_version(void) { return "0.1.0"; }
 
 const char *lgn_last_hip_error_string(void) {
     return g_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip);
+}
+
+void lgn_testing_set_arch(const char *arch) {
+    if (!arch) {
+        g_arch_overridden.store(false, std::memory_order_release);
+        return;
+    }
+    g_arch_overridden.store(false, std::memory_order_release);
+    strncpy(g_arch_override, arch, sizeof(g_arch_override) - 1);
+    g_arch_override[sizeof(g_arch_override) - 1] = '\0';
+    g_arch_overridden.store(true, std::memory_order_release);
+}
+
+void lgn_testing_fail_launches(int hip_error, int count) {
+    if (count <= 0 || hip_error == (int)hipSuccess) {
+        lgn::g_fail_launches.store(0, std::memory_order_relaxed);
+        return;
+    }
+    lgn::g_fail_error.store(hip_error, std::memory_order_relaxed);
+    lgn::g_fail_launches.store(count, std::memory_order_relaxed);
 }
 
 }  // extern "C"

@@ -1,6 +1,6 @@
-// lgn_fused_impl.hpp -- tile configuration table of the fused kernel and its
-// launcher, shared by the fp32 and bf16 instantiation units.
-#pragma once
+// lgn_fused.hip -- tile configuration table of the fused kernel, its
+// launcher, and the fp32 (v_mfma_f32_32x32x2_f32) and bf16
+// (v_mfma_f32_32x32x16_bf16) entry points behind lgn_forward_f32/_bf16.
 
 #include "lgn_fused.hpp"
 #include "lgn_launch.hpp"
@@ -33,8 +33,7 @@ hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     return launch_kernel(lgn_fused_kernel<DT, Cfg, CG, RING>, dim3((unsigned)blocks),
                          dim3(Cfg::NT), stream, x, W, b_lin, b_add, gamma, beta, M, K, N, eps,
-                         out, tiles_m, tiles_n, (float2 *)nullptr,
-                         (unsigned long long *)nullptr);
+                         out, tiles_m, tiles_n, (float2 *)nullptr);
 }
 
 // The LDS DMA ring needs K to be a multiple of its stage depth; any other K
@@ -97,6 +96,18 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
         default: return hipErrorInvalidValue;
     }
 #undef LGN_CASE
+}
+
+hipError_t launch_fused_f32(const float *x, const float *W, const float *b_lin,
+                            const float *b_add, const float *gamma, const float *beta, int M,
+                            int K, int N, int G, float eps, float *out, hipStream_t stream) {
+    return launch_fused<f32_t>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream);
+}
+
+hipError_t launch_fused_bf16(const uint16_t *x, const uint16_t *W, const float *b_lin,
+                             const float *b_add, const float *gamma, const float *beta, int M,
+                             int K, int N, int G, float eps, float *out, hipStream_t stream) {
+    return launch_fused<bf16_t>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream);
 }
 
 }  // namespace lgn

@@ -55,25 +55,14 @@ struct TileParams {
 // wide_part[row * (N / WC) + span]; a second kernel merges a group's spans and
 // normalises.  The epilogue keeps the per-sample-tile order of the normal
 // path: statistics, then that sample tile's stores.
-// PHASES (measurement probes only; off in every library instantiation): lane 0
-// of each wave records the shader clock at entry, after the main loop, after
-// the epilogue has issued its stores and after they have completed, plus the
-// 100 MHz real-time clock at entry and exit, into
-// phase_clk[(blockIdx.x * waves + wave) * 6 + 0..5].
-template <class DT, class Cfg, int CG, int RING, bool WIDE = false, bool PHASES = false>
+template <class DT, class Cfg, int CG, int RING, bool WIDE = false>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::OCC)))
 void lgn_fused_kernel(
     const typename dt_traits<DT>::storage *__restrict__ x,
     const typename dt_traits<DT>::storage *__restrict__ W, const float *__restrict__ b_lin,
     const float *__restrict__ b_add, const float *__restrict__ gamma,
     const float *__restrict__ beta, int M, int K, int N, float eps, float *__restrict__ out,
-    int tiles_m, int tiles_n, float2 *__restrict__ wide_part,
-    unsigned long long *__restrict__ phase_clk) {
-    [[maybe_unused]] unsigned long long clk0 = 0, real0 = 0, clk1 = 0;
-    if constexpr (PHASES) {
-        clk0 = __builtin_amdgcn_s_memtime();
-        real0 = __builtin_amdgcn_s_memrealtime();
-    }
+    int tiles_m, int tiles_n, float2 *__restrict__ wide_part) {
     static_assert(Cfg::BC % CG == 0, "groups must not straddle workgroup tiles");
     static_assert(!WIDE || CG == Cfg::WC, "the wide mode reduces each wave's channel span");
     constexpr int TS = Cfg::TS, TC = Cfg::TC;
@@ -122,7 +111,6 @@ void lgn_fused_kernel(
                 for (int j = 0; j < 4; ++j) acc[ts][tc][4 * q + j] = bl[j];
         }
     Sel::type::run(x, W, M, N, K, m0, n0, smem, tid, wc0, ws0, lr, h, acc);
-    if constexpr (PHASES) clk1 = __builtin_amdgcn_s_memtime();
 
     // ---- Swish, then the external bias (in registers) ----
     auto activate = [&](int ts) {
@@ -257,21 +245,6 @@ void lgn_fused_kernel(
         if constexpr (STAGED) __syncthreads();   // partials read before the block area is reused
 #pragma unroll
         for (int ts = 0; ts < TS; ++ts) finish(ts, &rstd[ts], &nmr[ts]);
-    }
-    if constexpr (PHASES) {
-        const unsigned long long clk2 = __builtin_amdgcn_s_memtime();
-        __builtin_amdgcn_s_waitcnt(0);   // every store of this wave has completed
-        const unsigned long long clk3 = __builtin_amdgcn_s_memtime();
-        const unsigned long long real3 = __builtin_amdgcn_s_memrealtime();
-        if (lane == 0) {
-            unsigned long long *p = phase_clk + ((size_t)blockIdx.x * (Cfg::NT / 64) + wave) * 6;
-            p[0] = clk0;
-            p[1] = clk1;
-            p[2] = clk2;
-            p[3] = clk3;
-            p[4] = real0;
-            p[5] = real3;
-        }
     }
 }
 

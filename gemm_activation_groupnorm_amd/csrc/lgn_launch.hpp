@@ -6,9 +6,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <tuple>
 
 namespace lgn {
+
+// Failure injection for the error-path tests (lgn_testing_fail_launches):
+// while fail_launches > 0, each launch decrements it and returns
+// fail_error instead of launching.
+inline std::atomic<int> g_fail_launches{0};
+inline std::atomic<int> g_fail_error{0};
+
+inline bool take_injected_failure(hipError_t &e) {
+    int n = g_fail_launches.load(std::memory_order_relaxed);
+    while (n > 0) {
+        if (g_fail_launches.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) {
+            e = (hipError_t)g_fail_error.load(std::memory_order_relaxed);
+            return true;
+        }
+    }
+    return false;
+}
 
 // Launches `kernel` with hipLaunchKernel and returns that call's own status
 // (not a sticky error left by some earlier runtime call).  Arguments are
@@ -17,6 +35,8 @@ template <typename... KArgs, typename... Args>
 hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
                          Args... args) {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    hipError_t injected;
+    if (take_injected_failure(injected)) return injected;
     std::tuple<KArgs...> packed(args...);
     void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
     std::apply([&](auto &...e) {
@@ -40,7 +60,7 @@ hipError_t launch_fused_bf16(const uint16_t *x, const uint16_t *W, const float *
                              int K, int N, int G, float eps, float *out, hipStream_t stream);
 
 // Groups wider than one tile (C = N/G a multiple of 256): the workspace
-// holds one (mean, M2) float pair per row and per 256-channel tile.
+// holds one (mean, M2) float pair per row and per 64 channels.
 hipError_t launch_wide_f32(const float *x, const float *W, const float *b_lin, const float *b_add,
                            const float *gamma, const float *beta, int M, int K, int N, int G,
                            float eps, float *out, void *workspace, hipStream_t stream);

@@ -78,14 +78,18 @@ __device__ __forceinline__ void block_merge(float &mean, float &m2, float &n, fl
 }
 
 // A chunk [start, end) of absolute element indices, split for 16-byte
-// accesses: a head of < 4 elements up to the first multiple of 4, a body of
-// whole float4s, and a tail of < 4 elements.  y and out are 16-byte aligned.
+// accesses: a head [start, a0) of < 4 elements up to the first multiple of 4,
+// a body [a0, a1) of whole float4s, and a tail [a1, end) of < 4 elements.
+// y and out are 16-byte aligned.  Both boundaries are clamped into the chunk,
+// so a chunk that holds no whole float4 is a head and a tail of < 4 each
+// (at most 3 + 3 elements then), and every element is covered exactly once.
 struct SghSplit {
     long long start, a0, a1, end;
     __device__ __forceinline__ SghSplit(long long s, long long e) : start(s), end(e) {
-        a0 = (s + 3) & ~3LL;
-        a1 = e & ~3LL;
-        if (a0 >= a1) a0 = a1 = e;   // no whole float4 inside: all head
+        const long long up = (s + 3) & ~3LL;
+        a0 = up < e ? up : e;
+        const long long dn = e & ~3LL;
+        a1 = dn > a0 ? dn : a0;
     }
     __device__ __forceinline__ int body4() const { return (int)((a1 - a0) >> 2); }
     // edge element handled by thread t (head: t < 4, tail: 64 <= t < 68), or -1

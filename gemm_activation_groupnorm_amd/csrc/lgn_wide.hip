@@ -1,6 +1,5 @@
-// lgn_wide_impl.hpp -- launcher of the wide-group forward, shared by the
-// fp32 and bf16 instantiation units.
-#pragma once
+// lgn_wide.hip -- launcher of the wide-group forward (groups wider than one
+// workgroup tile) and its fp32 and bf16 entry points.
 
 #include "lgn_launch.hpp"
 #include "lgn_wide.hpp"
@@ -31,19 +30,34 @@ hipError_t launch_wide(const typename dt_traits<DT>::storage *x,
         e = launch_kernel(lgn_fused_kernel<DT, Fast, kWideSpan, RING, true>,
                           dim3((unsigned)((long long)tiles_m * tiles_n)), dim3(Fast::NT), stream,
                           x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, tiles_m, tiles_n,
-                          part, (unsigned long long *)nullptr);
+                          part);
     } else {
         const int tiles_m = (M + Slow::BS - 1) / Slow::BS;
         e = launch_kernel(lgn_fused_kernel<DT, Slow, kWideSpan, 0, true>,
                           dim3((unsigned)((long long)tiles_m * tiles_n)), dim3(Slow::NT), stream,
                           x, W, b_lin, b_add, gamma, beta, M, K, N, eps, out, tiles_m, tiles_n,
-                          part, (unsigned long long *)nullptr);
+                          part);
     }
     if (e != hipSuccess) return e;
     const long long pairs = (long long)M * G;
     return launch_kernel(lgn_wide_norm_kernel<kWideSpan>, dim3((unsigned)((pairs + 3) / 4)),
                          dim3(256), stream, (const float2 *)part, gamma, beta, pairs, G,
                          (N / G) / kWideSpan, N / kWideSpan, eps, out);
+}
+
+hipError_t launch_wide_f32(const float *x, const float *W, const float *b_lin, const float *b_add,
+                           const float *gamma, const float *beta, int M, int K, int N, int G,
+                           float eps, float *out, void *workspace, hipStream_t stream) {
+    return launch_wide<f32_t>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+                              stream);
+}
+
+hipError_t launch_wide_bf16(const uint16_t *x, const uint16_t *W, const float *b_lin,
+                            const float *b_add, const float *gamma, const float *beta, int M,
+                            int K, int N, int G, float eps, float *out, void *workspace,
+                            hipStream_t stream) {
+    return launch_wide<bf16_t>(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+                               stream);
 }
 
 }  // namespace lgn

@@ -46,6 +46,8 @@ EXPORTS = (
     "lgn_status_string",
     "lgn_version",
     "lgn_last_hip_error_string",
+    "lgn_testing_set_arch",
+    "lgn_testing_fail_launches",
 )
 
 
@@ -98,6 +100,8 @@ def _load():
         ("lgn_status_string", [i], ctypes.c_char_p),
         ("lgn_version", [], ctypes.c_char_p),
         ("lgn_last_hip_error_string", [], ctypes.c_char_p),
+        ("lgn_testing_set_arch", [ctypes.c_char_p], None),
+        ("lgn_testing_fail_launches", [i, i], None),
     ):
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -108,12 +112,13 @@ def _load():
 _lib = _load()
 
 
-def _ptr(a, want: Optional[str]) -> Optional[int]:
-    """Device address of a tensor (checked dense and of dtype ``want``) or int."""
-    if a is None:
-        return None
-    if isinstance(a, int):
-        return a
+def _check(a, want: Optional[str], need: int) -> None:
+    """Checks one array argument: a tensor must be dense, of dtype ``want``
+    ("f32", "bf16", or None for a workspace of any dtype) and hold at least
+    ``need`` elements (bytes when ``want`` is None), so that the kernels never
+    address past its end.  An int is a raw device address and is not checked."""
+    if a is None or isinstance(a, int):
+        return
     import torch
     if not isinstance(a, torch.Tensor):
         raise TypeError("expected a torch.Tensor or an int address, got %r" % type(a))
@@ -123,7 +128,43 @@ def _ptr(a, want: Optional[str]) -> Optional[int]:
         raise ValueError("expected float32, got %s" % a.dtype)
     if want == "bf16" and a.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise ValueError("expected bfloat16 (or 16-bit raw bits), got %s" % a.dtype)
-    return a.data_ptr() if a.numel() > 0 else None
+    have = a.numel() * a.element_size() if want is None else a.numel()
+    if have < need:
+        raise ValueError("tensor holds %d %s, the call addresses %d"
+                         % (have, "bytes" if want is None else "elements", need))
+
+
+def _ptrs(*specs):
+    """Addresses of the array arguments, given as (array, want, need) triples.
+
+    Every array is checked (see _check) before any is converted; then every
+    tensor must be GPU memory, since the kernels dereference the address."""
+    for a, want, need in specs:
+        _check(a, want, need)
+    out = []
+    for a, _, _ in specs:
+        if a is None or isinstance(a, int):
+            out.append(a)
+            continue
+        if not a.is_cuda:
+            raise ValueError("tensor arguments must be on the GPU, got device %s" % a.device)
+        out.append(a.data_ptr() if a.numel() > 0 else None)
+    return out
+
+
+def _ptr(a, want: Optional[str], need: int = 0) -> Optional[int]:
+    """Address of one array argument (see _ptrs)."""
+    return _ptrs((a, want, need))[0]
+
+
+def _n(*dims) -> int:
+    """Element count of an array of these dimensions (0 if any is negative)."""
+    r = 1
+    for d in dims:
+        if d < 0:
+            return 0
+        r *= d
+    return r
 
 
 def _stream(stream) -> Optional[int]:
@@ -135,41 +176,53 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _fwd(dt, x, W, b_lin, b_add, gamma, beta, M, K, N, out, *workspace):
+    """Checked pointer arguments of the GroupNorm forward entry points:
+    x, W, b_lin, b_add, gamma, beta, out, then the workspace if one is given
+    as (workspace, workspace_bytes)."""
+    specs = [(x, dt, _n(M, K)), (W, dt, _n(N, K)), (b_lin, "f32", _n(N)), (b_add, "f32", _n(N)),
+             (gamma, "f32", _n(N)), (beta, "f32", _n(N)), (out, "f32", _n(M, N))]
+    if workspace:
+        specs.append((workspace[0], None, workspace[1]))
+    return _ptrs(*specs)
+
+
 def lgn_forward_f32(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream=None) -> int:
-    return _lib.lgn_forward_f32(_ptr(x, "f32"), _ptr(W, "f32"), _ptr(b_lin, "f32"),
-                                _ptr(b_add, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
-                                M, K, N, G, eps, _ptr(out, "f32"), _stream(stream))
+    px, pW, pbl, pba, pg, pb, po = _fwd("f32", x, W, b_lin, b_add, gamma, beta, M, K, N, out)
+    return _lib.lgn_forward_f32(px, pW, pbl, pba, pg, pb, M, K, N, G, eps, po, _stream(stream))
 
 
 def lgn_forward_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream=None) -> int:
-    return _lib.lgn_forward_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b_lin, "f32"),
-                                 _ptr(b_add, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
-                                 M, K, N, G, eps, _ptr(out, "f32"), _stream(stream))
+    px, pW, pbl, pba, pg, pb, po = _fwd("bf16", x, W, b_lin, b_add, gamma, beta, M, K, N, out)
+    return _lib.lgn_forward_bf16(px, pW, pbl, pba, pg, pb, M, K, N, G, eps, po, _stream(stream))
 
 
 def lgn_fused_supported(dtype: int, M: int, K: int, N: int, G: int) -> int:
     return _lib.lgn_fused_supported(dtype, M, K, N, G)
 
 
+def _fwd_ws(cfn, dt, x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+            workspace_bytes, stream) -> int:
+    px, pW, pbl, pba, pg, pb, po, pws = _fwd(dt, x, W, b_lin, b_add, gamma, beta, M, K, N, out,
+                                             workspace, workspace_bytes)
+    return cfn(px, pW, pbl, pba, pg, pb, M, K, N, G, eps, po, pws, workspace_bytes,
+               _stream(stream))
+
+
 def lgn_twopass_workspace_bytes(M: int, N: int) -> int:
     return _lib.lgn_twopass_workspace_bytes(M, N)
 
 
-def lgn_forward_twopass_f32(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
-                            workspace, workspace_bytes, stream=None) -> int:
-    return _lib.lgn_forward_twopass_f32(_ptr(x, "f32"), _ptr(W, "f32"), _ptr(b_lin, "f32"),
-                                        _ptr(b_add, "f32"), _ptr(gamma, "f32"),
-                                        _ptr(beta, "f32"), M, K, N, G, eps, _ptr(out, "f32"),
-                                        _ptr(workspace, None), workspace_bytes, _stream(stream))
+def lgn_forward_twopass_f32(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+                            workspace_bytes, stream=None) -> int:
+    return _fwd_ws(_lib.lgn_forward_twopass_f32, "f32", x, W, b_lin, b_add, gamma, beta, M, K, N,
+                   G, eps, out, workspace, workspace_bytes, stream)
 
 
-def lgn_forward_twopass_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
-                             workspace, workspace_bytes, stream=None) -> int:
-    return _lib.lgn_forward_twopass_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b_lin, "f32"),
-                                         _ptr(b_add, "f32"), _ptr(gamma, "f32"),
-                                         _ptr(beta, "f32"), M, K, N, G, eps, _ptr(out, "f32"),
-                                         _ptr(workspace, None), workspace_bytes,
-                                         _stream(stream))
+def lgn_forward_twopass_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
+                             workspace_bytes, stream=None) -> int:
+    return _fwd_ws(_lib.lgn_forward_twopass_bf16, "bf16", x, W, b_lin, b_add, gamma, beta, M, K,
+                   N, G, eps, out, workspace, workspace_bytes, stream)
 
 
 def lgn_wide_workspace_bytes(M: int, N: int) -> int:
@@ -178,34 +231,34 @@ def lgn_wide_workspace_bytes(M: int, N: int) -> int:
 
 def lgn_forward_wide_f32(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
                          workspace_bytes, stream=None) -> int:
-    return _lib.lgn_forward_wide_f32(_ptr(x, "f32"), _ptr(W, "f32"), _ptr(b_lin, "f32"),
-                                     _ptr(b_add, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
-                                     M, K, N, G, eps, _ptr(out, "f32"), _ptr(workspace, None),
-                                     workspace_bytes, _stream(stream))
+    return _fwd_ws(_lib.lgn_forward_wide_f32, "f32", x, W, b_lin, b_add, gamma, beta, M, K, N,
+                   G, eps, out, workspace, workspace_bytes, stream)
 
 
 def lgn_forward_wide_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, workspace,
                           workspace_bytes, stream=None) -> int:
-    return _lib.lgn_forward_wide_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b_lin, "f32"),
-                                      _ptr(b_add, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
-                                      M, K, N, G, eps, _ptr(out, "f32"), _ptr(workspace, None),
-                                      workspace_bytes, _stream(stream))
+    return _fwd_ws(_lib.lgn_forward_wide_bf16, "bf16", x, W, b_lin, b_add, gamma, beta, M, K, N,
+                   G, eps, out, workspace, workspace_bytes, stream)
 
 
 def lgn_lse_workspace_bytes(M: int, N: int) -> int:
     return _lib.lgn_lse_workspace_bytes(M, N)
 
 
+def _lse(cfn, dt, x, W, b, M, K, N, out, workspace, workspace_bytes, stream) -> int:
+    px, pW, pb, po, pws = _ptrs((x, dt, _n(M, K)), (W, dt, _n(N, K)), (b, "f32", _n(N)),
+                                (out, "f32", _n(M)), (workspace, None, workspace_bytes))
+    return cfn(px, pW, pb, M, K, N, po, pws, workspace_bytes, _stream(stream))
+
+
 def lgn_linear_lse_f32(x, W, b, M, K, N, out, workspace, workspace_bytes, stream=None) -> int:
-    return _lib.lgn_linear_lse_f32(_ptr(x, "f32"), _ptr(W, "f32"), _ptr(b, "f32"), M, K, N,
-                                   _ptr(out, "f32"), _ptr(workspace, None), workspace_bytes,
-                                   _stream(stream))
+    return _lse(_lib.lgn_linear_lse_f32, "f32", x, W, b, M, K, N, out, workspace,
+                workspace_bytes, stream)
 
 
 def lgn_linear_lse_bf16(x, W, b, M, K, N, out, workspace, workspace_bytes, stream=None) -> int:
-    return _lib.lgn_linear_lse_bf16(_ptr(x, "bf16"), _ptr(W, "bf16"), _ptr(b, "f32"), M, K, N,
-                                    _ptr(out, "f32"), _ptr(workspace, None), workspace_bytes,
-                                    _stream(stream))
+    return _lse(_lib.lgn_linear_lse_bf16, "bf16", x, W, b, M, K, N, out, workspace,
+                workspace_bytes, stream)
 
 
 def lgn_sgh_workspace_bytes(Nb: int, C: int, S: int, G: int) -> int:
@@ -214,9 +267,10 @@ def lgn_sgh_workspace_bytes(Nb: int, C: int, S: int, G: int) -> int:
 
 def lgn_swish_gn_hardswish_f32(y, gamma, beta, Nb, C, S, G, eps, out, workspace,
                                workspace_bytes, stream=None) -> int:
-    return _lib.lgn_swish_gn_hardswish_f32(_ptr(y, "f32"), _ptr(gamma, "f32"), _ptr(beta, "f32"),
-                                           Nb, C, S, G, eps, _ptr(out, "f32"),
-                                           _ptr(workspace, None), workspace_bytes,
+    py, pg, pb, po, pws = _ptrs((y, "f32", _n(Nb, C, S)), (gamma, "f32", _n(C)),
+                                (beta, "f32", _n(C)), (out, "f32", _n(Nb, C, S)),
+                                (workspace, None, workspace_bytes))
+    return _lib.lgn_swish_gn_hardswish_f32(py, pg, pb, Nb, C, S, G, eps, po, pws, workspace_bytes,
                                            _stream(stream))
 
 
@@ -226,10 +280,13 @@ def lgn_lnconv_workspace_bytes(B: int, C: int, L: int) -> int:
 
 def lgn_ln_gelu_conv1d_f32(x, ln_w, ln_b, conv_w, conv_b, B, C, L, dilation, eps, gelu_tanh, out,
                            workspace, workspace_bytes, stream=None) -> int:
-    return _lib.lgn_ln_gelu_conv1d_f32(_ptr(x, "f32"), _ptr(ln_w, "f32"), _ptr(ln_b, "f32"),
-                                       _ptr(conv_w, "f32"), _ptr(conv_b, "f32"), B, C, L,
-                                       dilation, eps, int(bool(gelu_tanh)), _ptr(out, "f32"),
-                                       _ptr(workspace, None), workspace_bytes, _stream(stream))
+    px, plw, plb, pcw, pcb, po, pws = _ptrs(
+        (x, "f32", _n(B, C, L)), (ln_w, "f32", _n(C, L)), (ln_b, "f32", _n(C, L)),
+        (conv_w, "f32", _n(C, C, 3)), (conv_b, "f32", _n(C)), (out, "f32", _n(B, C, L)),
+        (workspace, None, workspace_bytes))
+    return _lib.lgn_ln_gelu_conv1d_f32(px, plw, plb, pcw, pcb, B, C, L, dilation, eps,
+                                       int(bool(gelu_tanh)), po, pws, workspace_bytes,
+                                       _stream(stream))
 
 
 def lgn_status_string(status: int) -> str:
@@ -242,6 +299,16 @@ def lgn_version() -> str:
 
 def lgn_last_hip_error_string() -> str:
     return _lib.lgn_last_hip_error_string().decode()
+
+
+def lgn_testing_set_arch(arch: Optional[str]) -> None:
+    """Failure-path hook: compare this architecture name instead of the device's (None: undo)."""
+    _lib.lgn_testing_set_arch(None if arch is None else arch.encode())
+
+
+def lgn_testing_fail_launches(hip_error: int, count: int) -> None:
+    """Failure-path hook: the next `count` launches return `hip_error` instead of launching."""
+    _lib.lgn_testing_fail_launches(hip_error, count)
 
 
 def check(status: int) -> None:

@@ -241,6 +241,25 @@ const char *lgn_version(void);
  * thread ("no HIP error" if none).  Static storage; do not free. */
 const char *lgn_last_hip_error_string(void);
 
+/* ---- Failure-path hooks, for tests of the error paths above ----
+ * They let a test reach LGN_ERR_UNSUPPORTED (wrong device) and LGN_ERR_HIP
+ * (failed launch) without another GPU and without a faulty kernel.  Both are
+ * process-wide and not synchronised with calls running on other threads:
+ * set them while no entry point is in flight.
+ *
+ * lgn_testing_set_arch: while `arch` is non-NULL, every entry point's device
+ * check compares this architecture name (for example "gfx942") instead of
+ * querying the current device, and makes no HIP call for it; a name that does
+ * not start with "gfx950" then yields LGN_ERR_UNSUPPORTED.  The string is
+ * copied (at most 63 characters).  NULL restores the device query.
+ *
+ * lgn_testing_fail_launches: the next `count` kernel launches made by the
+ * library return `hip_error` (a hipError_t value other than hipSuccess)
+ * instead of launching, so the entry point returns LGN_ERR_HIP and
+ * lgn_last_hip_error_string() names that error.  count <= 0 clears it. */
+void lgn_testing_set_arch(const char *arch);
+void lgn_testing_fail_launches(int hip_error, int count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,7 +1,9 @@
 """fp64 CPU oracle for the fused Linear -> Swish -> +bias -> GroupNorm forward.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
-``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+``cpu_baseline`` leg of ``bench.py`` (which times this oracle and, with the same
+fp64 results, reports the error of every GPU output it times) may import this
+package.  It shares no code
 with the HIP library (``gemm_activation_groupnorm_amd``) and neither imports the
 other; the seeded input generators live in a module of their own.
 
@@ -64,6 +66,11 @@ _lib = None
 # Portable flags: the library travels to other x86-64 hosts, so no -march=native.
 # -ffp-contract=off keeps every multiply and add separately rounded.
 _CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
+# The host-tuned build timed as the CPU baseline: the same source and the same
+# IEEE semantics (no contraction, no reassociation), optimised for the host it
+# is compiled on, so it is built where it runs and never shipped.
+NATIVE_CFLAGS = ["-O3", "-march=native", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                 "-shared", "-fPIC"]
 
 
 def build(force: bool = False) -> str:
@@ -76,13 +83,27 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
-def _load():
+def use_native_build(dest_dir: str) -> str:
+    """Compile the oracle with NATIVE_CFLAGS into ``dest_dir`` and make every
+    function of this module use that build from now on; returns its path."""
+    global _lib
+    path = os.path.join(dest_dir, "liblgn_oracle_native.so")
+    subprocess.run(["gcc", *NATIVE_CFLAGS, "-o", path, _SRC, "-lm"], check=True)
+    with _lock:
+        _lib = None
+    _load(path)
+    return path
+
+
+def _load(path: str = None):
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
-                build()
-            lib = ctypes.CDLL(_LIB)
+            if path is None:
+                path = _LIB
+                if not os.path.exists(_LIB):
+                    build()
+            lib = ctypes.CDLL(path)
             dp = ctypes.POINTER(ctypes.c_double)
             L = ctypes.c_long
             lib.oracle_swish.argtypes = [ctypes.c_double]

@@ -70,3 +70,54 @@ def max_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
 
 def case(M, K, N, G, seed, dtype="f32", x_scale=1.0):
     return make_inputs(M, K, N, seed, dtype, x_scale)
+
+
+class ErrStats:
+    """Running error statistics of GPU output against the fp64 oracle over
+    every compared element: max abs, mean abs, and the count above the
+    tolerance.  Non-finite GPU values fail at once."""
+
+    def __init__(self, tol: float):
+        self.tol = tol
+        self.max = 0.0
+        self.sum = 0.0
+        self.n = 0
+        self.over = 0
+
+    def add(self, y_gpu: np.ndarray, y_ref: np.ndarray) -> None:
+        assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
+        if y_gpu.size == 0:
+            return
+        assert np.all(np.isfinite(y_gpu)), "non-finite GPU output"
+        d = np.abs(y_gpu.astype(np.float64) - y_ref)
+        self.max = max(self.max, float(d.max()))
+        self.sum += float(d.sum())
+        self.n += d.size
+        self.over += int(np.count_nonzero(d > self.tol))
+
+    @property
+    def mean(self) -> float:
+        return self.sum / self.n if self.n else 0.0
+
+    def summary(self) -> dict:
+        return {"elements": self.n, "max_abs": self.max, "mean_abs": self.mean,
+                "count_gt_tol": self.over, "tol": self.tol}
+
+    def __str__(self) -> str:
+        return ("max abs %.3e, mean abs %.3e, %d of %d elements > %.0e"
+                % (self.max, self.mean, self.over, self.n, self.tol))
+
+
+def compare_all_rows(outputs: dict, oracle_chunk, rows: int, tol: float,
+                     chunk: int = 2048) -> dict:
+    """Every element of each GPU output (host arrays whose first axis is the
+    row) against the oracle, computed once per chunk of rows:
+    oracle_chunk(r0, r1) returns the fp64 rows r0..r1-1.  Returns
+    {name: ErrStats}."""
+    stats = {k: ErrStats(tol) for k in outputs}
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        ref = oracle_chunk(r0, r1)
+        for k, y in outputs.items():
+            stats[k].add(y[r0:r1], ref)
+    return stats

@@ -297,3 +297,117 @@ def test_lnconv_unsupported(bad):
 
 def test_lnconv_empty_batch_is_a_no_op():
     assert _call_lnc(B=0, x=None, out=None, ws=None, ws_bytes=0) == lgn.LGN_OK
+
+
+# ---- the binding's own checks: device, size (before any C call) ----
+
+def _host_args(M=6, K=8, N=16, short=None):
+    """CPU tensors of the forward's sizes; `short` names one to make 1 element short."""
+    import torch
+    sizes = dict(x=M * K, W=N * K, b_lin=N, b_add=N, gamma=N, beta=N, out=M * N)
+    if short:
+        sizes[short] -= 1
+    return {k: torch.zeros(v, dtype=torch.float32) for k, v in sizes.items()}
+
+
+@pytest.mark.parametrize("short", [None, "x", "W", "b_lin", "b_add", "gamma", "beta", "out"])
+@pytest.mark.parametrize("fn", [lgn.lgn_forward_f32, lgn.lgn_forward_twopass_f32,
+                                lgn.lgn_forward_wide_f32], ids=lambda f: f.__name__)
+def test_binding_checks_sizes_then_device(fn, short):
+    import torch
+    M, K, N, G = 6, 8, 16, 2
+    a = _host_args(M, K, N, short)
+    args = [a["x"], a["W"], a["b_lin"], a["b_add"], a["gamma"], a["beta"], M, K, N, G, 1e-5,
+            a["out"]]
+    if fn is not lgn.lgn_forward_f32:
+        args += [torch.zeros(M * N), M * N * 4]
+    # an undersized tensor is named before anything else; a right-sized host
+    # tensor is refused because it is not device memory
+    with pytest.raises(ValueError, match="holds" if short else "on the GPU"):
+        fn(*args, stream=0)
+
+
+def test_binding_checks_workspace_bytes():
+    import torch
+    M, K, N, G = 6, 8, 16, 2
+    a = _host_args(M, K, N)
+    with pytest.raises(ValueError, match="holds 16 bytes, the call addresses 384"):
+        lgn.lgn_forward_twopass_f32(a["x"], a["W"], a["b_lin"], a["b_add"], a["gamma"], a["beta"],
+                                    M, K, N, G, 1e-5, a["out"], torch.zeros(4), M * N * 4,
+                                    stream=0)
+
+
+def test_binding_checks_other_entry_points():
+    import torch
+    z = lambda n: torch.zeros(n)
+    with pytest.raises(ValueError, match="holds"):
+        lgn.lgn_linear_lse_f32(z(6 * 8), z(16 * 8), z(16), 6, 8, 16, z(5), z(100), 400, stream=0)
+    with pytest.raises(ValueError, match="holds"):
+        lgn.lgn_swish_gn_hardswish_f32(z(2 * 4 * 9 - 1), z(4), z(4), 2, 4, 9, 2, 1e-5, z(72),
+                                       z(100), 400, stream=0)
+    with pytest.raises(ValueError, match="holds"):
+        lgn.lgn_ln_gelu_conv1d_f32(z(2 * 128 * 8), z(128 * 8), z(128 * 8), z(128 * 128 * 3 - 1),
+                                   z(128), 2, 128, 8, 1, 1e-5, 0, z(2 * 128 * 8), z(10), 40,
+                                   stream=0)
+    with pytest.raises(ValueError, match="on the GPU"):
+        lgn.lgn_linear_lse_f32(z(6 * 8), z(16 * 8), z(16), 6, 8, 16, z(6), z(100), 400, stream=0)
+
+
+# ---- failure paths: wrong device architecture, failed launch ----
+
+HIP_ERROR_LAUNCH_FAILURE = 719   # hipErrorLaunchFailure
+
+
+@pytest.fixture
+def arch_override():
+    yield lgn.lgn_testing_set_arch
+    lgn.lgn_testing_set_arch(None)
+    lgn.lgn_testing_fail_launches(0, 0)
+
+
+def _all_entry_points():
+    """(name, call) for every compute entry point, with valid shapes and fake addresses."""
+    calls = [(f.__name__, (lambda f=f: _call(f))) for f in FNS]
+    calls += [(f.__name__, (lambda f=f: _call_lse(f))) for f in LSE_FNS]
+    calls += [(f.__name__, (lambda f=f: f(A, A, A, A, A, A, 64, 32, 512, 2, 1e-5, A, A, 1 << 40,
+                                           stream=0)))
+              for f in (lgn.lgn_forward_wide_f32, lgn.lgn_forward_wide_bf16)]
+    calls.append(("lgn_swish_gn_hardswish_f32",
+                  lambda: lgn.lgn_swish_gn_hardswish_f32(A, A, A, 2, 16, 1000, 4, 1e-5, A, A,
+                                                         1 << 40, stream=0)))
+    calls.append(("lgn_ln_gelu_conv1d_f32",
+                  lambda: lgn.lgn_ln_gelu_conv1d_f32(A, A, A, A, A, 2, 128, 64, 4, 1e-5, 0,
+                                                     A + 1024, A, 1 << 40, stream=0)))
+    return calls
+
+
+@pytest.mark.parametrize("name,call", _all_entry_points(), ids=lambda v: v if isinstance(v, str) else "")
+def test_other_device_architecture_is_unsupported(arch_override, name, call):
+    # the device check compares the injected name and makes no HIP call
+    arch_override("gfx942")
+    assert call() == lgn.LGN_ERR_UNSUPPORTED
+    arch_override("gfx90a:sramecc+:xnack-")
+    assert call() == lgn.LGN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name,call", _all_entry_points(), ids=lambda v: v if isinstance(v, str) else "")
+def test_failed_launch_maps_to_hip_error(arch_override, name, call):
+    # the device check passes (injected gfx950) and the first kernel launch
+    # reports hipErrorLaunchFailure instead of launching: nothing reaches a GPU
+    arch_override("gfx950:sramecc+:xnack-")
+    lgn.lgn_testing_fail_launches(HIP_ERROR_LAUNCH_FAILURE, 1000)
+    assert call() == lgn.LGN_ERR_HIP
+    text = lgn.lgn_last_hip_error_string()
+    assert text != "no HIP error" and text
+    with pytest.raises(lgn.LgnError, match="LGN_ERR_HIP"):
+        lgn.check(lgn.LGN_ERR_HIP)
+
+
+def test_failure_injection_counts_down(arch_override):
+    arch_override("gfx950")
+    lgn.lgn_testing_fail_launches(HIP_ERROR_LAUNCH_FAILURE, 2)
+    assert _call(lgn.lgn_forward_f32) == lgn.LGN_ERR_HIP
+    assert _call(lgn.lgn_forward_bf16) == lgn.LGN_ERR_HIP
+    lgn.lgn_testing_fail_launches(0, 0)
+    # cleared: an argument error is still reported before any launch
+    assert _call(lgn.lgn_forward_f32, M=-1) == lgn.LGN_ERR_INVALID_ARG

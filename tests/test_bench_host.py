@@ -1,0 +1,53 @@
+"""bench.py's host-side pieces without a GPU: the error statistics of its
+check leg, the input hashes, the host description and the refusal of
+multi-GPU runs."""
+import hashlib
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_err_stats_counts_every_element():
+    st = bench.ErrStats(1e-3)
+    ref = np.zeros((3, 4))
+    y = np.zeros((3, 4), dtype=np.float32)
+    y[0, 0] = 2e-3
+    y[2, 3] = -5e-4
+    st.add(y[:2], ref[:2])
+    st.add(y[2:], ref[2:])
+    s = st.summary()
+    assert s["elements"] == 12 and s["count_gt_tol"] == 1 and s["nonfinite"] == 0
+    assert abs(s["max_abs_err"] - 2e-3) < 1e-9
+    assert abs(s["mean_abs_err"] - (2e-3 + 5e-4) / 12) < 1e-9
+
+
+def test_err_stats_flags_non_finite_output():
+    st = bench.ErrStats(1e-3)
+    y = np.array([0.0, np.nan, np.inf], dtype=np.float32)
+    st.add(y, np.zeros(3))
+    s = st.summary()
+    assert s["nonfinite"] == 2 and s["count_gt_tol"] == 2 and s["max_abs_err"] == np.inf
+
+
+def test_input_hashes_are_sha256_of_the_bytes():
+    a = np.arange(10, dtype=np.float32)
+    h = bench.sha256s({"a": a})
+    assert h["a"] == hashlib.sha256(a.tobytes()).hexdigest()
+
+
+def test_host_info_names_the_cpu():
+    hi = bench.host_info()
+    assert hi["logical_cpus"] == os.cpu_count() and hi["usable_cpus"] >= 1
+    assert hi["cpu_model"]
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""

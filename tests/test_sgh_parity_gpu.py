@@ -6,8 +6,8 @@ import torch
 
 import oracle
 from gemm_activation_groupnorm_amd import lgn
-from gemm_activation_groupnorm_amd.inputs import SGH_WORKLOADS, make_sgh_inputs, sample_rows
-from gpu_helpers import TOL, log
+from gemm_activation_groupnorm_amd.inputs import SGH_WORKLOADS, make_sgh_inputs
+from gpu_helpers import TOL, compare_all_rows, log
 
 pytestmark = pytest.mark.gpu
 
@@ -83,15 +83,50 @@ def test_sgh_constant_group_gives_hardswish_beta():
 
 
 @pytest.mark.parametrize("wi", range(len(SGH_WORKLOADS)))
-def test_sgh_full_size_sampled(wi):
+def test_sgh_full_size_every_element(wi):
     w = SGH_WORKLOADS[wi]
     log("sgh workload %s" % w.name)
     inp = make_sgh_inputs(w.Nb, w.C, w.S, w.seed)
     out = run_sgh(dev(inp), w.Nb, w.C, w.S, w.G, w.eps)
     torch.cuda.synchronize()
-    rows = sample_rows(w.Nb, 4, seed=w.seed)   # whole samples: their groups are complete
-    ref = oracle.swish_gn_hardswish(inp["y"][rows], inp["gamma"], inp["beta"], w.G, w.eps)
-    err = _err(out[torch.from_numpy(rows).cuda()].cpu().numpy(), ref)
-    log("  sampled-sample max abs err %.3e" % err)
+    host = out.cpu().numpy()
+    del out
+    # whole samples at a time (their groups are complete), every element
+    stats = compare_all_rows(
+        {"sgh": host},
+        lambda r0, r1: oracle.swish_gn_hardswish(inp["y"][r0:r1], inp["gamma"], inp["beta"],
+                                                 w.G, w.eps),
+        w.Nb, TOL["f32"], chunk=16)
+    log("  every element: %s" % stats["sgh"])
+    assert stats["sgh"].n == w.elements and stats["sgh"].max <= TOL["f32"]
+
+
+# Chunks with no whole 16-byte float4 inside them: a group whose length
+# leaves 5 or 6 elements in its last chunk, starting 1 or 2 elements past a
+# 16-byte boundary, must still cover every element exactly once (head and
+# tail of up to 3 each).
+EDGE_SHAPES = [
+    (1, 2, 5, 2),        # groups of 5 elements starting at 0 and 5
+    (2, 4, 5, 4),        # 8 groups of 5: starts 0, 5, 10, ... cover every residue mod 4
+    (2, 16, 16389, 16),  # last chunk of each group holds 5 elements
+    (3, 6, 16390, 3),    # last chunk of 6 elements, groups of 2 channels
+    (1, 3, 7, 3),        # groups of 7 starting at 0, 7, 14
+]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "Nb%d_C%d_S%d_G%d" % s)
+def test_sgh_chunks_without_a_whole_float4(shape):
+    Nb, C, S, G = shape
+    log("sgh edge case Nb=%d C=%d S=%d G=%d" % shape)
+    inp = make_sgh_inputs(Nb, C, S, 800 + Nb + C + S + G)
+    d = dev(inp)
+    # the output starts as NaN: an element the kernels skip stays NaN and fails
+    out = torch.full((Nb, C, S), float("nan"), dtype=torch.float32, device="cuda")
+    run_sgh(d, Nb, C, S, G, 1e-5, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got)), "elements left unwritten"
+    ref = oracle.swish_gn_hardswish(inp["y"], inp["gamma"], inp["beta"], G, 1e-5)
+    err = _err(got, ref)
+    log("  max abs err %.3e" % err)
     assert err <= TOL["f32"]
-    assert bool(torch.isfinite(out).all())
