@@ -134,6 +134,26 @@ lgn_status forward_wide(const T *x, const T *W, const float *b_lin, const float 
                                           gamma, beta, M, K, N, G, eps, out, workspace, stream));
 }
 
+// The wide forward with the library's own scratch in place of the caller's
+// workspace: no allocation of any kind (for callers that cannot allocate).
+lgn_status forward_wide_noalloc(const float *x, const float *W, const float *b_lin,
+                                const float *b_add, const float *gamma, const float *beta,
+                                int M, int K, int N, int G, float eps, float *out,
+                                hipStream_t stream) {
+    lgn_status s = validate(DT_F32, x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out);
+    if (s != LGN_OK || M == 0) return s;
+    if ((N / G) % 256 != 0) return LGN_ERR_UNSUPPORTED;
+    if (!aligned(gamma, 16) || !aligned(beta, 16)) return LGN_ERR_UNSUPPORTED;
+    if (lgn_wide_workspace_bytes(M, N) > lgn::kWideScratchBytes) return LGN_ERR_TOO_LARGE;
+    s = check_device();
+    if (s != LGN_OK) return s;
+    void *ws = nullptr;
+    hipError_t e = lgn::wide_scratch_address(&ws);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(lgn::launch_wide_f32(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
+                                         ws, stream));
+}
+
 template <int DT, class T>
 lgn_status linear_lse(const T *x, const T *W, const float *b, int M, int K, int N, float *out,
                       void *workspace, size_t ws_bytes, hipStream_t stream) {
@@ -222,6 +242,14 @@ lgn_status lgn_forward_wide_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const flo
                                  workspace_bytes, stream);
 }
 
+lgn_status lgn_forward_wide_f32_noalloc(const float *x, const float *W, const float *b_lin,
+                                        const float *b_add, const float *gamma,
+                                        const float *beta, int M, int K, int N, int G, float eps,
+                                        float *out, hipStream_t stream) {
+    static_assert(lgn::kWideScratchBytes == LGN_WIDE_NOALLOC_SCRATCH_BYTES, "header limit");
+    return forward_wide_noalloc(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out, stream);
+}
+
 size_t lgn_lse_workspace_bytes(int M, int N) {
     if (M <= 0 || N <= 0) return 0;
     const size_t tiles = ((size_t)N + lgn::kLseTileChannels - 1) / lgn::kLseTileChannels;
@@ -306,6 +334,9 @@ const char *lgn_status_string(lgn_status s) {
                    "(16-byte aligned x/W/out, N % 4 == 0, K % 4 (fp32) or K % 8 (bf16) == 0; "
                    "fused: N/G a power of two in 8..1024)";
         case LGN_ERR_HIP: return "LGN_ERR_HIP: a HIP runtime call or kernel launch failed";
+        case LGN_ERR_TOO_LARGE:
+            return "LGN_ERR_TOO_LARGE: the call needs more scratch than the no-allocation entry "
+                   "point holds (LGN_WIDE_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown lgn_status";
     }
 }

@@ -68,6 +68,11 @@ hipError_t launch_wide_bf16(const uint16_t *x, const uint16_t *W, const float *b
                             const float *b_add, const float *gamma, const float *beta, int M,
                             int K, int N, int G, float eps, float *out, void *workspace,
                             hipStream_t stream);
+// The library-held scratch that replaces that workspace in the entry point
+// that allocates nothing: its size, and its device address on the current
+// device (looked up on the first call on each device).
+constexpr size_t kWideScratchBytes = (size_t)32 << 20;
+hipError_t wide_scratch_address(void **addr);
 
 // Linear -> logsumexp -> LeakyReLU x2 -> GELU x2.  The workspace holds one
 // (max, sum) float pair per row and per tile of this many channels.

@@ -4,9 +4,48 @@
 #include "lgn_launch.hpp"
 #include "lgn_wide.hpp"
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace lgn {
+
+// Scratch of the no-allocation entry point (lgn_forward_wide_f32_noalloc):
+// the per-(row, 64-channel span) (mean, M2) partials that the other wide
+// entry points keep in the caller's workspace.  Every GPU the library runs on
+// holds its own copy for the life of the process; every call on one GPU
+// shares it.  Host code never passes `scratch` itself to a kernel (on the
+// host it only names the symbol): it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kWideScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_addr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t wide_scratch_address(void **addr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // first call on this device, with the device current: look the
+        // symbol up once and keep its address
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *addr = p;
+    return hipSuccess;
+}
 
 // Kernel 1 is the fused kernel's 256 x 256 tile (same core and schedules as
 // its C <= 64 case) in WIDE mode; K not a multiple of the stage depth takes

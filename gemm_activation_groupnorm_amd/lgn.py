@@ -21,6 +21,9 @@ LGN_OK = 0
 LGN_ERR_INVALID_ARG = 1
 LGN_ERR_UNSUPPORTED = 2
 LGN_ERR_HIP = 3
+LGN_ERR_TOO_LARGE = 4
+# scratch held by the library for lgn_forward_wide_f32_noalloc (include/lgn.h)
+WIDE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -36,6 +39,7 @@ EXPORTS = (
     "lgn_wide_workspace_bytes",
     "lgn_forward_wide_f32",
     "lgn_forward_wide_bf16",
+    "lgn_forward_wide_f32_noalloc",
     "lgn_lse_workspace_bytes",
     "lgn_linear_lse_f32",
     "lgn_linear_lse_bf16",
@@ -89,6 +93,7 @@ def _load():
         ("lgn_wide_workspace_bytes", [i, i], sz),
         ("lgn_forward_wide_f32", two, i),
         ("lgn_forward_wide_bf16", two, i),
+        ("lgn_forward_wide_f32_noalloc", fwd, i),
         ("lgn_lse_workspace_bytes", [i, i], sz),
         ("lgn_linear_lse_f32", lse, i),
         ("lgn_linear_lse_bf16", lse, i),
@@ -239,6 +244,13 @@ def lgn_forward_wide_bf16(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
                           workspace_bytes, stream=None) -> int:
     return _fwd_ws(_lib.lgn_forward_wide_bf16, "bf16", x, W, b_lin, b_add, gamma, beta, M, K, N,
                    G, eps, out, workspace, workspace_bytes, stream)
+
+
+def lgn_forward_wide_f32_noalloc(x, W, b_lin, b_add, gamma, beta, M, K, N, G, eps, out,
+                                 stream=None) -> int:
+    px, pW, pbl, pba, pg, pb, po = _fwd("f32", x, W, b_lin, b_add, gamma, beta, M, K, N, out)
+    return _lib.lgn_forward_wide_f32_noalloc(px, pW, pbl, pba, pg, pb, M, K, N, G, eps, po,
+                                             _stream(stream))
 
 
 def lgn_lse_workspace_bytes(M: int, N: int) -> int:

@@ -50,7 +50,9 @@ enum {
                                 workspace too small */
     LGN_ERR_UNSUPPORTED = 2, /* device is not gfx950, or a shape/alignment outside what the
                                 kernels cover (see each entry point) */
-    LGN_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+    LGN_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+    LGN_ERR_TOO_LARGE = 4    /* the no-allocation entry point's scratch is too small for
+                                the call */
 };
 
 /* Raw bfloat16 bits: the upper 16 bits of an IEEE binary32. */
@@ -230,6 +232,31 @@ lgn_status lgn_forward_wide_bf16(const lgn_bf16 *x, const lgn_bf16 *W,
                                  int M, int K, int N, int G, float eps,
                                  float *out, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as lgn_forward_wide_f32, with the (mean, M2) partials kept in a
+ * scratch array that the library holds for the life of the process instead of
+ * a caller workspace.  The call allocates nothing (no hipMalloc, no library
+ * allocation); the caller still passes x, W, the vectors and out.
+ *
+ * Limit: the call needs lgn_wide_workspace_bytes(M, N) (8 bytes per row per
+ * 64 channels) of scratch; above LGN_WIDE_NOALLOC_SCRATCH_BYTES (32 MiB, for
+ * example M * N up to 2^31 elements) it returns LGN_ERR_TOO_LARGE before any
+ * HIP call.  Every GPU the library runs on holds its own copy of the scratch
+ * (32 MiB of device memory each), and every call on one GPU shares it: calls
+ * that overlap in time on one GPU (different streams, or threads) race on it
+ * and give wrong results; serialise them.  The scratch needs no clearing:
+ * each call writes every partial before reading it.  Other rules, errors and
+ * results (bitwise equal to lgn_forward_wide_f32 on the same inputs) as for
+ * lgn_forward_wide_f32. */
+#define LGN_WIDE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+lgn_status lgn_forward_wide_f32_noalloc(const float *x, const float *W,
+                                        const float *b_lin, const float *b_add,
+                                        const float *gamma, const float *beta,
+                                        int M, int K, int N, int G, float eps,
+                                        float *out, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *lgn_status_string(lgn_status s);

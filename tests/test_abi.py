@@ -411,3 +411,49 @@ def test_failure_injection_counts_down(arch_override):
     lgn.lgn_testing_fail_launches(0, 0)
     # cleared: an argument error is still reported before any launch
     assert _call(lgn.lgn_forward_f32, M=-1) == lgn.LGN_ERR_INVALID_ARG
+
+
+# ---- the entry point that allocates nothing ----
+
+def _call_noalloc(**kw):
+    a = dict(x=A, W=A, b_lin=A, b_add=A, gamma=A, beta=A, out=A, M=64, K=32, N=512, G=2,
+             eps=1e-5)
+    a.update(kw)
+    return lgn.lgn_forward_wide_f32_noalloc(a["x"], a["W"], a["b_lin"], a["b_add"], a["gamma"],
+                                            a["beta"], a["M"], a["K"], a["N"], a["G"], a["eps"],
+                                            a["out"], stream=0)
+
+
+def test_noalloc_limit_matches_header():
+    text = open(os.path.join(ROOT, "include", "lgn.h")).read()
+    m = re.search(r"#define LGN_WIDE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == lgn.WIDE_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    # 8 bytes per row per 64 channels: 32768 x 16384 needs 64 MiB > 32 MiB
+    need = lgn.lgn_wide_workspace_bytes(32768, 16384)
+    assert need > lgn.WIDE_NOALLOC_SCRATCH_BYTES
+    assert _call_noalloc(M=32768, N=16384, G=16) == lgn.LGN_ERR_TOO_LARGE
+    # the largest row count that fits at N = 16384
+    fit = lgn.WIDE_NOALLOC_SCRATCH_BYTES // (16384 // 64 * 8)
+    assert lgn.lgn_wide_workspace_bytes(fit, 16384) == lgn.WIDE_NOALLOC_SCRATCH_BYTES
+    assert _call_noalloc(M=fit + 1, N=16384, G=16) == lgn.LGN_ERR_TOO_LARGE
+    assert lgn.lgn_status_string(lgn.LGN_ERR_TOO_LARGE).startswith("LGN_ERR_TOO_LARGE")
+
+
+@pytest.mark.parametrize("bad", INVALID, ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
+def test_noalloc_invalid_arguments(bad):
+    kw = dict(bad)
+    if kw.get("N") == 128 and kw.get("G") == 3:
+        kw = dict(N=512, G=3)
+    assert _call_noalloc(**kw) == lgn.LGN_ERR_INVALID_ARG
+
+
+def test_noalloc_unsupported_and_empty(arch_override):
+    assert _call_noalloc(N=384, G=3) == lgn.LGN_ERR_UNSUPPORTED       # 128-channel groups
+    assert _call_noalloc(K=6) == lgn.LGN_ERR_UNSUPPORTED
+    assert _call_noalloc(gamma=A + 4) == lgn.LGN_ERR_UNSUPPORTED
+    assert _call_noalloc(M=0, x=None, out=None) == lgn.LGN_OK
+    arch_override("gfx942")
+    assert _call_noalloc() == lgn.LGN_ERR_UNSUPPORTED
