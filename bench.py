@@ -131,7 +131,7 @@ class Telemetry:
     every `interval` seconds in a background thread, and summarises the
     samples that fall inside each named window (the timed regions)."""
 
-    def __init__(self, interval: float = 0.02):
+    def __init__(self, interval: float = 0.01):
         self.interval = interval
         self.samples = []          # (t, sclk_mhz or None, power_w or None)
         self.windows = {}          # name -> (t0, t1)
@@ -162,7 +162,13 @@ class Telemetry:
                 for f in ("power1_average", "power1_input"):
                     if power is None and os.path.exists(os.path.join(dd, f)):
                         power = os.path.join(dd, f)
-        self.source = {"pci": pci, "sclk": sclk, "power": power}
+        if sclk is None:
+            # no hwmon clock: the current DPM level of pp_dpm_sclk ("N: 2100Mhz *")
+            dpm = os.path.join("/sys/bus/pci/devices", pci, "pp_dpm_sclk")
+            if os.path.exists(dpm):
+                sclk = dpm
+        cap = self._read(os.path.join(os.path.dirname(power), "power1_cap"), 1e-6) if power else None
+        self.source = {"pci": pci, "sclk": sclk, "power": power, "power_cap_w": cap}
         return sclk, power
 
     @staticmethod
@@ -171,8 +177,14 @@ class Telemetry:
             return None
         try:
             with open(path) as f:
-                return int(f.read().strip()) * scale
-        except (OSError, ValueError):
+                text = f.read()
+            if path.endswith("pp_dpm_sclk"):
+                for line in text.splitlines():
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("M")[0].split("m")[0])
+                return None
+            return int(text.strip()) * scale
+        except (OSError, ValueError, IndexError):
             return None
 
     def _run(self):

@@ -24,8 +24,8 @@ and raises AssertionError when it disagrees with:
   ln N, order inside a row does not matter, rows are independent; a negative
   logsumexp passes through both LeakyReLUs as 1e-4 times itself.
 
-``tests/test_lse_oracle_mutants.py`` plants one plausible mistake at a time in
-a numpy re-implementation and shows that each one fails at least one check.
+``tests/test_lse_oracle_pins.py`` also plants one plausible mistake at a time
+in a numpy re-implementation and shows that each one fails at least one check.
 """
 from __future__ import annotations
 
