@@ -53,10 +53,11 @@ template <> struct dt_traits<bf16_t> {
 //      next stage's first reads hide under that whole chunk pair (needs a
 //      ring of at least 3 stages and an even number of chunk pairs).
 // EARLY (PIPE >= 1) = sample tiles whose MFMAs are issued before those reads
-// (0: reads first).
+// (0: reads first).  GM = sample tiles per band of the tile order (tile_coords).
 template <class DT, int BS_, int BC_, int WAVES_S_, int WAVES_C_, int ROWB_, int OCC_ = 1,
-          int PIPE_ = 1, int EARLY_ = 1>
+          int PIPE_ = 1, int EARLY_ = 1, int GM_ = 8>
 struct TileCfg {
+    static constexpr int GM = GM_;
     static constexpr int BS = BS_, BC = BC_, WAVES_S = WAVES_S_, WAVES_C = WAVES_C_;
     static constexpr int ROWB = ROWB_;
     static constexpr int OCC = OCC_;
@@ -624,21 +625,31 @@ struct BlockStore {
                 *reinterpret_cast<f32x4 *>(blk + lr * (CPRW * 16) + 16 * (chunk ^ (lr & 15))) =
                     value(tc, q);
             }
+        // one base address per lane; block row i*RPI lies i*RPI*N floats further on
+        const int r0 = lane / CPRW, chunk = lane % CPRW;
+        float *base = out + (size_t)(row0 + r0) * (size_t)N + (col0 + 4 * chunk);
+        auto put = [&](f32x4 *dst, const f32x4 &y) {
+            if constexpr (STREAM)
+                __builtin_nontemporal_store(y, dst);
+            else
+                *dst = y;
+        };
+        auto get = [&](int i) {
+            const int row = RPI * i + r0;
+            return *reinterpret_cast<const f32x4 *>(blk + row * (CPRW * 16) +
+                                                    16 * (chunk ^ (row & 15)));
+        };
+        if (row0 + 32 <= M && col0 + WC <= N) {
+            // the whole block lies inside out (the wave-uniform common case): no checks
 #pragma unroll
-        for (int i = 0; i < 32 / RPI; ++i) {
-            const int row = RPI * i + lane / CPRW;
-            const int chunk = lane % CPRW;
-            const f32x4 y = *reinterpret_cast<const f32x4 *>(blk + row * (CPRW * 16) +
-                                                             16 * (chunk ^ (row & 15)));
-            const int m = row0 + row;
-            const int c = col0 + 4 * chunk;
-            if (m < M && c < N) {
-                f32x4 *dst = reinterpret_cast<f32x4 *>(out + (size_t)m * (size_t)N + c);
-                if constexpr (STREAM)
-                    __builtin_nontemporal_store(y, dst);
-                else
-                    *dst = y;
-            }
+            for (int i = 0; i < 32 / RPI; ++i)
+                put(reinterpret_cast<f32x4 *>(base + (size_t)(i * RPI) * (size_t)N), get(i));
+        } else {
+            const bool col_ok = col0 + 4 * chunk < N;
+#pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i)
+                if (col_ok && row0 + RPI * i + r0 < M)
+                    put(reinterpret_cast<f32x4 *>(base + (size_t)(i * RPI) * (size_t)N), get(i));
         }
     }
 };

@@ -91,7 +91,7 @@ void lgn_fused_kernel(
     const int wc0 = wcI * Cfg::WC;
 
     int tm, tn;
-    tile_coords<8>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_coords<Cfg::GM>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * Cfg::BS;
     const int n0 = tn * Cfg::BC;
 

@@ -44,6 +44,8 @@ SHAPES = [
     (100, 16, 12),       # fewer channels than one wave's span
     (300, 96, 1000),
     (70, 256, 8192),     # the transcript's feature count
+    (129, 192, 520),     # bf16: three 64-deep stages (the ring's depth), ragged tiles
+    (200, 640, 2048),    # bf16: ten 64-deep stages
 ]
 
 
@@ -93,15 +95,16 @@ def test_lse_full_size_every_row(wi):
     assert st.n == w.M and st.max <= TOL[w.dtype]
 
 
-def test_lse_deterministic_and_row_split():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lse_deterministic_and_row_split(dtype):
     M, K, N = 513, 128, 4096
-    inp = make_inputs(M, K, N, 88, "f32")
-    dev = to_device(inp, "f32")
-    y1 = run_lse(dev, M, K, N, "f32")
-    y2 = run_lse(dev, M, K, N, "f32")
+    inp = make_inputs(M, K, N, 88, dtype)
+    dev = to_device(inp, dtype)
+    y1 = run_lse(dev, M, K, N, dtype)
+    y2 = run_lse(dev, M, K, N, dtype)
     h = 200
-    ya = run_lse(dict(dev, x=dev["x"][:h].contiguous()), h, K, N, "f32")
-    yb = run_lse(dict(dev, x=dev["x"][h:].contiguous()), M - h, K, N, "f32")
+    ya = run_lse(dict(dev, x=dev["x"][:h].contiguous()), h, K, N, dtype)
+    yb = run_lse(dict(dev, x=dev["x"][h:].contiguous()), M - h, K, N, dtype)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2), "run-to-run difference"
     assert torch.equal(torch.cat([ya, yb]), y1), "row split changes results"
