@@ -272,7 +272,7 @@ size_t lgn_sgh_workspace_bytes(int Nb, int C, long long S, int G) {
     if (Nb <= 0 || C <= 0 || S <= 0 || G <= 0 || C % G != 0) return 0;
     const long long L = (long long)(C / G) * S;
     if (L > 0x7fffffffLL) return 0;
-    return (size_t)Nb * (size_t)G * (size_t)lgn::sgh_parts(L) * 2 * sizeof(float);
+    return lgn::sgh_workspace_bytes(Nb, C, S, G);
 }
 
 size_t lgn_lnconv_workspace_bytes(int B, int C, int L) {
@@ -356,6 +356,11 @@ void lgn_testing_set_arch(const char *arch) {
     strncpy(g_arch_override, arch, sizeof(g_arch_override) - 1);
     g_arch_override[sizeof(g_arch_override) - 1] = '\0';
     g_arch_overridden.store(true, std::memory_order_release);
+}
+
+void lgn_testing_set_sgh_spin_limit(int polls) {
+    lgn::g_sgh_spin_limit.store(polls < 0 ? lgn::kSghSpinLimit : polls,
+                                std::memory_order_relaxed);
 }
 
 void lgn_testing_fail_launches(int hip_error, int count) {

@@ -85,6 +85,11 @@ hipError_t launch_linear_lse_bf16(const uint16_t *x, const uint16_t *W, const fl
 // Swish -> spatial GroupNorm -> HardSwish.  The workspace holds one
 // (mean, M2) float pair per chunk of kSghChunk elements of every group.
 long long sgh_parts(long long group_elems);
+size_t sgh_workspace_bytes(int Nb, int C, long long S, int G);
+// Polls of the single-pass kernel's bounded wait before it forms the group's
+// statistics itself (lgn_testing_set_sgh_spin_limit).
+constexpr int kSghSpinLimit = 1 << 16;
+inline std::atomic<int> g_sgh_spin_limit{kSghSpinLimit};
 
 // LayerNorm -> GELU -> dilated Conv1d -> + input (C % 128 == 0, L % 4 == 0,
 // dilation 1..16).  The workspace holds the packed weights

@@ -52,6 +52,7 @@ EXPORTS = (
     "lgn_last_hip_error_string",
     "lgn_testing_set_arch",
     "lgn_testing_fail_launches",
+    "lgn_testing_set_sgh_spin_limit",
 )
 
 
@@ -107,6 +108,7 @@ def _load():
         ("lgn_last_hip_error_string", [], ctypes.c_char_p),
         ("lgn_testing_set_arch", [ctypes.c_char_p], None),
         ("lgn_testing_fail_launches", [i, i], None),
+        ("lgn_testing_set_sgh_spin_limit", [i], None),
     ):
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -321,6 +323,12 @@ def lgn_testing_set_arch(arch: Optional[str]) -> None:
 def lgn_testing_fail_launches(hip_error: int, count: int) -> None:
     """Failure-path hook: the next `count` launches return `hip_error` instead of launching."""
     _lib.lgn_testing_fail_launches(hip_error, count)
+
+
+def lgn_testing_set_sgh_spin_limit(polls: int) -> None:
+    """Failure-path hook: polls of the single-pass spatial GroupNorm's bounded wait
+    before it forms the group's statistics itself (negative: the default)."""
+    _lib.lgn_testing_set_sgh_spin_limit(polls)
 
 
 def check(status: int) -> None:

@@ -156,8 +156,12 @@ lgn_status lgn_linear_lse_bf16(const lgn_bf16 *x, const lgn_bf16 *W, const float
  *   out[n,c,i] = hardswish((s - mean) / sqrt(var + eps) * gamma[c] + beta[c])
  *
  * Layouts: y and out [Nb][C][S] dense (NCDHW); gamma, beta [C] fp32.  `out`
- * may be `y` itself (in place) but must not overlap it otherwise.  Two
- * kernels: per-chunk statistics into `workspace`, then the apply pass;
+ * may be `y` itself (in place) but must not overlap it otherwise.  Out of
+ * place, with groups of at most 256 chunks of 16384 elements, one kernel
+ * reads y once: each workgroup holds its chunk, publishes the chunk's
+ * statistics, waits (bounded) for the rest of its group and writes its chunk.
+ * In place or with larger groups, two kernels: per-chunk statistics into
+ * `workspace`, then the apply pass.  Both give bitwise the same output.
  * `workspace` must hold lgn_sgh_workspace_bytes(Nb, C, S, G) bytes (8 per
  * 16384-element chunk of every group), be 8-byte aligned and overlap nothing
  * else.  Rules: Nb >= 0 (0 is a no-op), C >= 1, S >= 1, G >= 1, C % G == 0,
@@ -283,9 +287,15 @@ const char *lgn_last_hip_error_string(void);
  * lgn_testing_fail_launches: the next `count` kernel launches made by the
  * library return `hip_error` (a hipError_t value other than hipSuccess)
  * instead of launching, so the entry point returns LGN_ERR_HIP and
- * lgn_last_hip_error_string() names that error.  count <= 0 clears it. */
+ * lgn_last_hip_error_string() names that error.  count <= 0 clears it.
+ *
+ * lgn_testing_set_sgh_spin_limit: the number of polls the single-pass
+ * spatial GroupNorm kernel makes for the rest of its group before it forms
+ * the group's statistics itself (bitwise the same result, by another route);
+ * 0 takes that route at once, a negative value restores the default. */
 void lgn_testing_set_arch(const char *arch);
 void lgn_testing_fail_launches(int hip_error, int count);
+void lgn_testing_set_sgh_spin_limit(int polls);
 
 #ifdef __cplusplus
 }

@@ -130,3 +130,57 @@ def test_sgh_chunks_without_a_whole_float4(shape):
     err = _err(got, ref)
     log("  max abs err %.3e" % err)
     assert err <= TOL["f32"]
+
+
+# ---- the single-pass form against the two-kernel form ----
+#
+# Out of place (and at most 256 chunks per group) the call runs one kernel
+# that reads y once; in place it runs the statistics and apply kernels.
+# Both must give bitwise the same output, and so must the single-pass
+# kernel's own fallback (statistics formed from y when its bounded wait for
+# the rest of the group runs out), forced here with a wait of zero polls.
+
+ONEPASS_SHAPES = [
+    (2, 16, 123039 // 37, 4),    # odd S, groups off 16-byte boundaries
+    (3, 6, 16390, 3),            # a 6-element last chunk per group
+    (4, 16, 777, 16),            # one channel per group
+    (1, 8, 16384 * 9 + 3, 2),    # 37 chunks per group
+    (2, 2048, 5, 2),             # 1024 channels per group (the 1024 coefficient table)
+    (1, 16384, 2, 2),            # 8192 channels per group (the 8192 coefficient table)
+]
+
+
+@pytest.mark.parametrize("shape", ONEPASS_SHAPES, ids=lambda s: "Nb%d_C%d_S%d_G%d" % s)
+def test_sgh_single_pass_equals_two_kernels_and_its_fallback(shape):
+    Nb, C, S, G = shape
+    log("sgh single pass vs two kernels Nb=%d C=%d S=%d G=%d" % shape)
+    inp = make_sgh_inputs(Nb, C, S, 900 + Nb + C + S + G)
+    d = dev(inp)
+    one = run_sgh(d, Nb, C, S, G, 1e-5)                      # out of place: single pass
+    buf = d["y"].clone()
+    run_sgh(dict(d, y=buf), Nb, C, S, G, 1e-5, out=buf)      # in place: two kernels
+    try:
+        lgn.lgn_testing_set_sgh_spin_limit(0)
+        fb = run_sgh(d, Nb, C, S, G, 1e-5)                   # single pass, fallback route
+        torch.cuda.synchronize()
+    finally:
+        lgn.lgn_testing_set_sgh_spin_limit(-1)
+    assert torch.equal(one, buf), "single pass differs from the two-kernel path"
+    assert torch.equal(one, fb), "single pass differs from its fallback route"
+    ref = oracle.swish_gn_hardswish(inp["y"], inp["gamma"], inp["beta"], G, 1e-5)
+    err = _err(one.cpu().numpy(), ref)
+    log("  bitwise equal on all three routes; max abs err %.3e" % err)
+    assert err <= TOL["f32"]
+
+
+def test_sgh_groups_beyond_the_single_pass_take_two_kernels():
+    # 257 chunks per group: over the single-pass limit, the two-kernel path
+    Nb, C, S, G = 1, 1, 16384 * 256 + 7, 1
+    log("sgh 257-chunk group")
+    inp = make_sgh_inputs(Nb, C, S, 41)
+    out = run_sgh(dev(inp), Nb, C, S, G, 1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.swish_gn_hardswish(inp["y"], inp["gamma"], inp["beta"], G, 1e-5)
+    err = _err(out.cpu().numpy(), ref)
+    log("  max abs err %.3e" % err)
+    assert err <= TOL["f32"]
