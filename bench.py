@@ -542,32 +542,51 @@ def check_outputs(wl: Workload, recs: list) -> None:
                   st.tol, time.perf_counter() - t0))
 
 
-def cpu_baseline(wl: Workload, seconds: float, tmpdir: str) -> dict:
-    """The oracle, compiled with -O3 -march=native on this host, timed on the
-    first rows of the workload (about `seconds` of work; OpenMP over rows on
-    every host thread), as GEMM TFLOP/s of its fp64 arithmetic."""
+def cpu_baseline(wl: Workload, variant: str, seconds: float, tmpdir: str) -> dict:
+    """The oracle of the headline's method, compiled with -O3 -march=native on
+    this host, timed on the first rows (samples) of the workload -- about
+    `seconds` of work, OpenMP on every host thread -- and scaled to the
+    headline's unit: GEMM (or convolution) TFLOP/s of its fp64 arithmetic, or
+    GB/s of the spatial GroupNorm tail's algorithmic bytes."""
     import oracle
     path = oracle.use_native_build(tmpdir)
     w, i = wl.w, wl.inp
-    args = (i["b_lin"], i["b_add"], i["gamma"], i["beta"], w.G, w.eps)
-    probe = min(w.M, 64)
+    if wl.kind == "sgh":
+        total, probe, what = w.Nb, 1, "samples"
+        run = lambda n: oracle.swish_gn_hardswish(i["y"][:n], i["gamma"], i["beta"], w.G, w.eps)
+        per_unit, unit, scale = 2.0 * w.C * w.S * 4, "GB/s", 1e9
+    elif wl.kind == "lnconv":
+        total, probe, what = w.B, 1, "samples"
+        run = lambda n: oracle.ln_gelu_conv1d(i["x"][:n], i["ln_w"], i["ln_b"], i["conv_w"],
+                                              i["conv_b"], w.dilation, w.eps,
+                                              gelu_tanh=w.gelu_tanh)
+        per_unit, unit, scale = w.flops / w.B, "TFLOP/s", 1e12
+    elif variant == "lse":
+        total, probe, what = w.M, min(w.M, 16), "rows"
+        run = lambda n: oracle.linear_lse_forward(i["x"][:n], i["W"], i["b_lin"])
+        per_unit, unit, scale = 2.0 * w.N * w.K, "TFLOP/s", 1e12
+    else:
+        total, probe, what = w.M, min(w.M, 64), "rows"
+        run = lambda n: oracle.lgn_forward(i["x"][:n], i["W"], i["b_lin"], i["b_add"],
+                                           i["gamma"], i["beta"], w.G, w.eps)
+        per_unit, unit, scale = 2.0 * w.N * w.K, "TFLOP/s", 1e12
     t0 = time.perf_counter()
-    oracle.lgn_forward(i["x"][:probe], i["W"], *args)
-    per_row = (time.perf_counter() - t0) / probe
-    rows = int(max(probe, min(w.M, seconds / max(per_row, 1e-9))))
+    run(probe)
+    per = (time.perf_counter() - t0) / probe
+    n = int(max(probe, min(total, seconds / max(per, 1e-9))))
     t0 = time.perf_counter()
-    oracle.lgn_forward(i["x"][:rows], i["W"], *args)
+    run(n)
     dt = time.perf_counter() - t0
-    flops = 2.0 * rows * w.N * w.K
     hi = host_info()
     return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
+        "value": per_unit * n / dt / scale,
+        "unit": unit,
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": "first %d of %d rows of %s, fp64 C oracle built with %s, %.1f s wall, %d "
-                  "OpenMP threads on %s" % (rows, w.M, w.name, " ".join(oracle.NATIVE_CFLAGS[:2]),
-                                            dt, oracle.num_threads(), hi["cpu_model"]),
+        "sample": "first %d of %d %s of %s, fp64 C oracle built with %s, %.1f s wall, %d "
+                  "OpenMP threads on %s" % (n, total, what, w.name,
+                                            " ".join(oracle.NATIVE_CFLAGS[:2]), dt,
+                                            oracle.num_threads(), hi["cpu_model"]),
         "cpu_model": hi["cpu_model"],
         "build": os.path.basename(path),
     }
@@ -763,9 +782,8 @@ def main():
         for wl, recs in measured:
             check_outputs(wl, recs)
         res["check"] = head_rec["check"]
-        if head_wl.kind == "gemm" and head_rec["variant"] != "lse":
-            with tempfile.TemporaryDirectory() as td:
-                res["cpu_baseline"] = cpu_baseline(head_wl, args.cpu_seconds, td)
+        with tempfile.TemporaryDirectory() as td:
+            res["cpu_baseline"] = cpu_baseline(head_wl, head_rec["variant"], args.cpu_seconds, td)
             eprint("[bench] cpu baseline: %s" % res["cpu_baseline"]["sample"])
     for r in extra:
         for k in [k for k in r if k.startswith("_")]:

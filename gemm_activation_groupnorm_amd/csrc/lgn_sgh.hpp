@@ -372,10 +372,11 @@ __global__ __launch_bounds__(kSghThreads) void lgn_sgh_apply_kernel(
 // Single-pass form (out must not overlap y): grid = groups * parts, one
 // workgroup per chunk, group by group in blockIdx order.  Workgroups are
 // dealt to the 8 XCDs in turn, so a group's chunks spread over all of them
-// and the whole GPU holds about 32 groups of P2's shape at a time: only the
-// group being dispatched at the moment waits long.  (Keeping each group on
-// one XCD instead left about 4 groups per XCD in flight and measured 0.548 ms
-// against 0.415 ms at 128 x 16 x 31 x 63 x 63.  Placement decides speed only.)
+// and the whole GPU holds about 32 groups at a time (4 channels x 31 x 63 x
+// 63 each): only the group being dispatched at the moment waits long.
+// (Keeping each group on one XCD instead left about 4 groups per XCD in
+// flight and measured 0.548 ms against 0.415 ms at 128 x 16 x 31 x 63 x 63.
+// Placement decides speed only.)
 //
 // A workgroup loads its chunk once and keeps the Swish values in registers.
 // It publishes the chunk's (mean, M2) as ONE 64-bit atomic store into

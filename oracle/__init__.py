@@ -95,6 +95,15 @@ def use_native_build(dest_dir: str) -> str:
     return path
 
 
+def use_default_build() -> str:
+    """Undo use_native_build: go back to the portable ``liblgn_oracle.so``."""
+    global _lib
+    with _lock:
+        _lib = None
+    _load()
+    return _LIB
+
+
 def _load(path: str = None):
     global _lib
     with _lock:

@@ -41,7 +41,7 @@
 #include <omp.h>
 #endif
 
-/* Linear layer, one row (P1 problem statement; weight stored as
+/* Linear layer, one row (Kimi-K2.6 l2_p37, problem statement; weight stored as
  * [out_features, in_features] like nn.Linear):
  *   z[n] = sum_{k=0}^{K-1} x[k] * W[n][k] + b_lin[n]                       */
 static void linear_row(const double *xrow, const double *W, const double *b_lin,
@@ -65,7 +65,8 @@ double oracle_swish(double z)
 }
 
 /* GroupNorm of one row of N channels split into G contiguous groups of
- * C = N / G channels (P1: "channels for a group are contiguous").  Mean and
+ * C = N / G channels, group g holding channels g*C .. g*C + C - 1 (Kimi-K2.6
+ * l2_p37, its GroupNorm discussion of how channels map to groups).  Mean and
  * population variance (divide by C) per group, eps added to the variance
  * inside the square root, then per-channel gamma/beta.  Exact two-pass.
  * mean_out / var_out, if non-NULL, receive the G per-group statistics.     */

@@ -1,6 +1,6 @@
 """bench.py's host-side pieces without a GPU: the error statistics of its
-check leg, the input hashes, the host description and the refusal of
-multi-GPU runs."""
+check leg, the input hashes, the host description, the CPU-baseline leg of
+every headline variant and the refusal of multi-GPU runs."""
 import hashlib
 import os
 import subprocess
@@ -51,3 +51,35 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
+
+
+def _fake(kind, w, inp):
+    """A stand-in for bench.Workload: its host inputs and shape, no device."""
+    import types
+    return types.SimpleNamespace(kind=kind, w=w, inp=inp, name=w.name)
+
+
+def _baseline_cases():
+    from gemm_activation_groupnorm_amd import inputs as I
+    gw = I.Workload("tiny_f32", 64, 32, 128, 8, "f32", 0)
+    sw = I.SghWorkload("tiny_sgh", 3, 8, 2, 3, 5, 2, 7)
+    cw = I.LnConvWorkload("tiny_lnconv", 2, 8, 16, 2, 9)
+    return [
+        ("gemm", "fused", gw, I.workload_inputs(gw), "TFLOP/s", "rows"),
+        ("gemm", "lse", gw, I.workload_inputs(gw), "TFLOP/s", "rows"),
+        ("sgh", "sgh", sw, I.make_sgh_inputs(sw.Nb, sw.C, sw.S, sw.seed), "GB/s", "samples"),
+        ("lnconv", "lnconv", cw, I.make_lnconv_inputs(cw.B, cw.C, cw.L, cw.seed), "TFLOP/s",
+         "samples"),
+    ]
+
+
+def test_cpu_baseline_covers_every_headline_variant(tmp_path):
+    import oracle
+    try:
+        for kind, variant, w, inp, unit, what in _baseline_cases():
+            cb = bench.cpu_baseline(_fake(kind, w, inp), variant, 0.05, str(tmp_path))
+            assert cb["unit"] == unit and cb["kind"] == "oracle", (variant, cb)
+            assert cb["value"] > 0 and cb["cores"] >= 1
+            assert (" %s of %s," % (what, w.name)) in cb["sample"]
+    finally:
+        oracle.use_default_build()
