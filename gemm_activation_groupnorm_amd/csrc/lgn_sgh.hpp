@@ -402,8 +402,11 @@ __device__ __forceinline__ unsigned long long sgh_pack(float mean, float m2) {
            ((unsigned long long)__float_as_uint(m2) << 32);
 }
 
+// Occupancy: 4 waves per SIMD (128 VGPRs); the MAXCG = 8192 instance's 66 KiB
+// of LDS allows 2 workgroups per CU, so it asks for 2.
 template <int MAXCG>
-__global__ __launch_bounds__(kSghThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kSghThreads)
+__attribute__((amdgpu_waves_per_eu(MAXCG > 1024 ? 2 : 4)))
 void lgn_sgh_onepass_kernel(
     const float *__restrict__ y, const float *__restrict__ gamma,
     const float *__restrict__ beta, int C, long long S, int G, int parts, float eps,
