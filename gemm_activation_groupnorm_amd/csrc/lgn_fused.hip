@@ -21,6 +21,7 @@ namespace lgn {
 //               bf16: 128 x 512, 2 x 4 waves of 64 x 128, ring of 3
 //   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128 (8 waves per group), ring of 2;
 //                fp32 with the simple schedule (fragments read right before their MFMAs)
+//                and bands of 16 sample tiles
 // and register-staged tiles for any other K.
 template <class DT, class Cfg, int CG, int RING>
 hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
@@ -76,9 +77,11 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
     constexpr int R128 = BF ? 4 : 3;
     typedef typename std::conditional<BF, TileCfg<DT, 128, 512, 2, 4, 64, 2>,
                                       TileCfg<DT, 64, 512, 1, 4, 64>>::type F512;
-    // fp32: simple schedule; bf16: fragments read under the MFMAs
+    // fp32: simple schedule, bands of 16 sample tiles (the same time as bands
+    // of 8 at 16384 x 2048 x 8192, with 1.61 GB fetched beyond L2 per launch
+    // instead of 2.42 GB); bf16: fragments read under the MFMAs
     typedef typename std::conditional<BF, TileCfg<DT, 64, 1024, 1, 8, 64, 1, 1>,
-                                      TileCfg<DT, 64, 1024, 1, 8, 64, 1, 0>>::type F1024;
+                                      TileCfg<DT, 64, 1024, 1, 8, 64, 1, 0, 1, 16>>::type F1024;
     const int cg = N / G;
 #define LGN_CASE(C, FAST, RING, SLOW)                                                            \
     case C:                                                                                     \

@@ -3,6 +3,8 @@
 #include "lgn_launch.hpp"
 #include "lgn_twopass.hpp"
 
+#include <type_traits>
+
 namespace lgn {
 
 template <class DT, class Cfg, int RING>
@@ -18,15 +20,21 @@ static hipError_t launch_gemm_bias_cfg(const typename dt_traits<DT>::storage *x,
                          dim3(Cfg::NT), stream, x, W, b_lin, M, K, N, z, tiles_m, tiles_n);
 }
 
-// 256 x 128 tiles of 4 waves (128 x 64 each): the LDS DMA ring when K is a
-// multiple of its stage depth, else the register-staged core.
+// The fused kernel's 256 x 256 tile (8 waves of 128 x 64; fp32: ring of 3,
+// bf16: ring of 4 with the mid-stage barrier) when K is a multiple of its
+// stage depth, else the register-staged core.  The GEMM-only kernel measured
+// 1.94-2.55 ms (fp32) and 0.311 ms (bf16) on this tile at 32768 x 1024 x
+// 4096, against 2.23-2.34 ms and 0.351 ms on 256 x 128 tiles of 4 waves;
+// z is bitwise the same.
 template <class DT>
 static hipError_t launch_gemm_bias(const typename dt_traits<DT>::storage *x,
                                    const typename dt_traits<DT>::storage *W, const float *b_lin,
                                    int M, int K, int N, float *z, hipStream_t stream) {
-    typedef TileCfg<DT, 256, 128, 2, 2, 64, 2> Fast;
+    constexpr bool BF = std::is_same<DT, bf16_t>::value;
+    typedef typename std::conditional<BF, TileCfg<DT, 256, 256, 2, 4, 64, 2, 2, 2>,
+                                      TileCfg<DT, 256, 256, 2, 4, 64, 2>>::type Fast;
     typedef TileCfg<DT, 128, 128, 2, 2, 128, 2> Slow;
-    constexpr int RING = 3;
+    constexpr int RING = BF ? 4 : 3;
     if (K % Fast::BK == 0)
         return launch_gemm_bias_cfg<DT, Fast, RING>(x, W, b_lin, M, K, N, z, stream);
     return launch_gemm_bias_cfg<DT, Slow, 0>(x, W, b_lin, M, K, N, z, stream);

@@ -27,7 +27,7 @@ void lgn_gemm_bias_kernel(
     const int ws0 = (wave / Cfg::WAVES_C) * Cfg::WS;
     const int wc0 = (wave % Cfg::WAVES_C) * Cfg::WC;
     int tm, tn;
-    tile_coords<8>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_coords<Cfg::GM>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * Cfg::BS;
     const int n0 = tn * Cfg::BC;
 
