@@ -14,7 +14,9 @@ human-readable summary goes to stderr.
 value      : GEMM TFLOP/s of the whole timed region, 2*M*N*K*K_steps / wall time.
 roofline   : the kernel's mean time per launch from one HIP event pair recorded
              on the launch stream around the timed launches, against the MI355X
-             dense MFMA peak of its input type (fp32 157.3, bf16 2500 TFLOP/s).
+             dense MFMA peak of its input type (fp32 157.3, bf16 2500 TFLOP/s);
+             frac_at_sclk divides by that peak scaled to the median shader
+             clock of the timed region (the peaks are quoted at 2400 MHz).
              traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
              counters (profiles/traffic.json), only if the kernel sources are
              unchanged since the counters were taken, else null.
@@ -38,6 +40,7 @@ import sys
 import tempfile
 import threading
 import time
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -45,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused Linear+Swish+bias+GroupNorm TFLOP/s at M32768 K1024 N4096; % MFMA peak"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 HBM_PEAK_GBPS = 8000.0
+PEAK_SCLK_MHZ = 2400.0      # the shader clock the MFMA peaks are quoted at
 TOL = {"f32": 2e-4, "bf16": 3e-2}
 DEFAULT_WORKLOAD = "m32768_k1024_n4096_g64_f32"
 
@@ -219,6 +223,16 @@ class Telemetry:
                 out[key] = {"min": round(v[0], 1), "median": round(v[len(v) // 2], 1),
                             "max": round(v[-1], 1)}
         return out
+
+
+def frac_at_clock(achieved: float, peak: float, telemetry) -> Optional[float]:
+    """achieved / (peak scaled to the median shader clock of the timed
+    region), or None without a clock reading."""
+    try:
+        mhz = telemetry["sclk_mhz"]["median"]
+    except (TypeError, KeyError):
+        return None
+    return round(achieved / (peak * mhz / PEAK_SCLK_MHZ), 4) if mhz else None
 
 
 # --------------------------------------------------------------- timing ----
@@ -470,6 +484,9 @@ def measure(wl: Workload, variant: str, steps: int, warmup: int, tel: Telemetry,
     if per_launch:
         rec["per_launch"] = r.distributions()
     rec["telemetry"] = tel.summary(key)
+    if wl.kind != "sgh":
+        rec["frac_of_peak_at_sclk"] = frac_at_clock(rec["tflops"], PEAK_TFLOPS[wl.dtype],
+                                                    rec["telemetry"])
     rec["_host"] = r.host_output()
     eprint("[bench] %s: %.3f ms/step, kernel mean %.4f ms -> %s" % (key, wall / steps * 1e3,
                                                                     kmean, msg))
@@ -552,28 +569,28 @@ def cpu_baseline(wl: Workload, variant: str, seconds: float, tmpdir: str) -> dic
     path = oracle.use_native_build(tmpdir)
     w, i = wl.w, wl.inp
     if wl.kind == "sgh":
-        total, probe, what = w.Nb, 1, "samples"
+        total, trial, what = w.Nb, 1, "samples"
         run = lambda n: oracle.swish_gn_hardswish(i["y"][:n], i["gamma"], i["beta"], w.G, w.eps)
         per_unit, unit, scale = 2.0 * w.C * w.S * 4, "GB/s", 1e9
     elif wl.kind == "lnconv":
-        total, probe, what = w.B, 1, "samples"
+        total, trial, what = w.B, 1, "samples"
         run = lambda n: oracle.ln_gelu_conv1d(i["x"][:n], i["ln_w"], i["ln_b"], i["conv_w"],
                                               i["conv_b"], w.dilation, w.eps,
                                               gelu_tanh=w.gelu_tanh)
         per_unit, unit, scale = w.flops / w.B, "TFLOP/s", 1e12
     elif variant == "lse":
-        total, probe, what = w.M, min(w.M, 16), "rows"
+        total, trial, what = w.M, min(w.M, 16), "rows"
         run = lambda n: oracle.linear_lse_forward(i["x"][:n], i["W"], i["b_lin"])
         per_unit, unit, scale = 2.0 * w.N * w.K, "TFLOP/s", 1e12
     else:
-        total, probe, what = w.M, min(w.M, 64), "rows"
+        total, trial, what = w.M, min(w.M, 64), "rows"
         run = lambda n: oracle.lgn_forward(i["x"][:n], i["W"], i["b_lin"], i["b_add"],
                                            i["gamma"], i["beta"], w.G, w.eps)
         per_unit, unit, scale = 2.0 * w.N * w.K, "TFLOP/s", 1e12
     t0 = time.perf_counter()
-    run(probe)
-    per = (time.perf_counter() - t0) / probe
-    n = int(max(probe, min(total, seconds / max(per, 1e-9))))
+    run(trial)
+    per = (time.perf_counter() - t0) / trial
+    n = int(max(trial, min(total, seconds / max(per, 1e-9))))
     t0 = time.perf_counter()
     run(n)
     dt = time.perf_counter() - t0
@@ -662,7 +679,8 @@ def headline_json(wl: Workload, rec: dict, args) -> dict:
                 "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
                              "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                              "traffic": traffic_for(w.name, "sgh"),
-                             "kernel_ms_mean": round(kmean, 4), "kernel": "sgh stats+apply"}}
+                             "kernel_ms_mean": round(kmean, 4),
+                             "kernel": "lgn_sgh_clear_kernel+lgn_sgh_onepass_kernel"}}
     ach = w.flops / (kmean * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     if wl.kind == "lnconv":
@@ -682,7 +700,8 @@ def headline_json(wl: Workload, rec: dict, args) -> dict:
             "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                          "traffic": traffic_for(w.name, rec["variant"]),
-                         "kernel_ms_mean": round(kmean, 4), "kernel": kernel}}
+                         "kernel_ms_mean": round(kmean, 4), "kernel": kernel,
+                         "frac_at_sclk": frac_at_clock(ach, peak, rec.get("telemetry"))}}
 
 
 def main():

@@ -83,3 +83,11 @@ def test_cpu_baseline_covers_every_headline_variant(tmp_path):
             assert (" %s of %s," % (what, w.name)) in cb["sample"]
     finally:
         oracle.use_default_build()
+
+
+def test_fraction_at_the_measured_clock():
+    tel = {"samples": 3, "sclk_mhz": {"min": 1800.0, "median": 1800.0, "max": 1800.0}}
+    # 900 of a 2500 peak quoted at 2400 MHz: at 1800 MHz the peak is 1875
+    assert bench.frac_at_clock(900.0, 2500.0, tel) == 0.48
+    assert bench.frac_at_clock(900.0, 2500.0, {"samples": 0}) is None
+    assert bench.frac_at_clock(900.0, 2500.0, None) is None
