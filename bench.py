@@ -525,7 +525,16 @@ class ErrStats:
 
 def check_outputs(wl: Workload, recs: list) -> None:
     """Compares every element of each record's output with the oracle (one
-    oracle pass per chunk of rows, shared by the workload's records)."""
+    oracle pass per chunk of rows, shared by the workload's records of the
+    same method)."""
+    lse = [r for r in recs if r["variant"] == "lse"]
+    rest = [r for r in recs if r["variant"] != "lse"]
+    for group in (lse, rest):
+        if group:
+            _check_group(wl, group)
+
+
+def _check_group(wl: Workload, recs: list) -> None:
     import oracle
     t0 = time.perf_counter()
     w, i = wl.w, wl.inp
@@ -538,11 +547,10 @@ def check_outputs(wl: Workload, recs: list) -> None:
         ref_of = lambda a, b: oracle.ln_gelu_conv1d(i["x"][a:b], i["ln_w"], i["ln_b"],
                                                     i["conv_w"], i["conv_b"], w.dilation, w.eps,
                                                     gelu_tanh=w.gelu_tanh)
-    elif all(r["variant"] == "lse" for r in recs):
+    elif recs[0]["variant"] == "lse":
         rows, chunk = w.M, 256
         ref_of = lambda a, b: oracle.linear_lse_forward(i["x"][a:b], i["W"], i["b_lin"])
     else:
-        assert not any(r["variant"] == "lse" for r in recs)
         rows, chunk = w.M, 2048
         ref_of = lambda a, b: oracle.lgn_forward(i["x"][a:b], i["W"], i["b_lin"], i["b_add"],
                                                  i["gamma"], i["beta"], w.G, w.eps)
@@ -712,10 +720,11 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", default="fused",
                     choices=["fused", "twopass", "wide", "lse", "sgh", "lnconv"],
-                    help="lse: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2 (use with an "
-                         "m1024_k8192_n8192_lse_* workload); sgh: Swish -> spatial GroupNorm -> "
-                         "HardSwish (reports GB/s); lnconv: LayerNorm -> GELU -> dilated "
-                         "Conv1d -> + x (these two pick their own workload by default)")
+                    help="lse: Linear -> logsumexp -> LeakyReLU x2 -> GELU x2; sgh: Swish -> "
+                         "spatial GroupNorm -> HardSwish (reports GB/s); lnconv: LayerNorm -> "
+                         "GELU -> dilated Conv1d -> + x.  Without --workload these three take "
+                         "their own default workload (m1024_k8192_n8192_lse_f32, "
+                         "n128_c16_d31_h63_w63_g4_sgh_f32, b32_c256_l4096_d4_lnconv_f32)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg: no CPU baseline and no per-line check")
     ap.add_argument("--no-extra", action="store_true",
@@ -757,7 +766,7 @@ def main():
 
     tel = Telemetry().start()
     head_name, head_var = args.workload, args.variant
-    if head_var in ("sgh", "lnconv") and args.workload == DEFAULT_WORKLOAD:
+    if head_var in ("sgh", "lnconv", "lse") and args.workload == DEFAULT_WORKLOAD:
         head_name = [n for n, v in EXTRA if head_var in v][0]
     groups = [(head_name, [head_var])]
     if not args.no_extra:

@@ -91,3 +91,22 @@ def test_fraction_at_the_measured_clock():
     assert bench.frac_at_clock(900.0, 2500.0, tel) == 0.48
     assert bench.frac_at_clock(900.0, 2500.0, {"samples": 0}) is None
     assert bench.frac_at_clock(900.0, 2500.0, None) is None
+
+
+def test_check_leg_splits_methods_sharing_a_workload(monkeypatch):
+    """A workload timed with both the GroupNorm forward and the logsumexp
+    method: each record is compared with its own method's oracle."""
+    import types
+    from gemm_activation_groupnorm_amd import inputs as I
+    import oracle
+    w = I.Workload("tiny_f32", 64, 32, 128, 8, "f32", 0)
+    inp = I.workload_inputs(w)
+    wl = types.SimpleNamespace(kind="gemm", w=w, inp=inp, name=w.name, dtype="f32")
+    fwd = oracle.lgn_forward(inp["x"], inp["W"], inp["b_lin"], inp["b_add"], inp["gamma"],
+                             inp["beta"], w.G, w.eps).astype(np.float32)
+    lse = oracle.linear_lse_forward(inp["x"], inp["W"], inp["b_lin"]).astype(np.float32)
+    recs = [{"variant": "lse", "_host": lse}, {"variant": "fused", "_host": fwd},
+            {"variant": "twopass", "_host": fwd}]
+    bench.check_outputs(wl, recs)
+    for r in recs:
+        assert r["check"]["count_gt_tol"] == 0 and r["check"]["elements"] == r["_host"].size
