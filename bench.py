@@ -225,14 +225,20 @@ class Telemetry:
         return out
 
 
+MIN_CLOCK_SAMPLES = 5
+
+
 def frac_at_clock(achieved: float, peak: float, telemetry) -> Optional[float]:
     """achieved / (peak scaled to the median shader clock of the timed
-    region), or None without a clock reading."""
+    region), or None without at least MIN_CLOCK_SAMPLES clock readings."""
     try:
         mhz = telemetry["sclk_mhz"]["median"]
+        n = telemetry["samples"]
     except (TypeError, KeyError):
         return None
-    return round(achieved / (peak * mhz / PEAK_SCLK_MHZ), 4) if mhz else None
+    if not mhz or n < MIN_CLOCK_SAMPLES:
+        return None
+    return round(achieved / (peak * mhz / PEAK_SCLK_MHZ), 4)
 
 
 # --------------------------------------------------------------- timing ----
@@ -245,7 +251,10 @@ class _Timed:
         duration from one HIP event pair on the launch stream around them.
         `warmup` untimed launches first; with min_warm_ms > 0 the warm-up goes
         on until that much GPU time has passed (the clocks ramp up under load
-        over tens of milliseconds).  Returns (wall, mean_ms, t0, t1)."""
+        over tens of milliseconds).  Returns (wall, mean_ms, w0, t1): the
+        telemetry window [w0, t1] is the timed region plus up to the last
+        100 ms of warm-up (the same launches, clocks settled), since a short
+        timed region alone holds too few sysfs samples."""
         import torch
         t_warm = time.perf_counter()
         for _ in range(warmup):
@@ -264,7 +273,7 @@ class _Timed:
         end.record(self.stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        return t1 - t0, start.elapsed_time(end) / steps, t0, t1
+        return t1 - t0, start.elapsed_time(end) / steps, max(t_warm, t0 - 0.1), t1
 
     def distribution(self, launches: int = 50, flush_bytes: int = 0):
         """Per-launch durations (one HIP event pair around each launch on the
@@ -669,6 +678,24 @@ EXTRA = [
 ]
 
 
+METHOD_NAMES = {
+    "fused": "fused Linear+Swish+bias+GroupNorm",
+    "twopass": "two-pass Linear+Swish+bias+GroupNorm (GEMM, then the GroupNorm epilogue kernel)",
+    "wide": "wide-group Linear+Swish+bias+GroupNorm (fused tile, then the normalise kernel)",
+    "lse": "Linear->logsumexp->LeakyReLU x2->GELU x2",
+}
+
+
+def gemm_metric(w, variant: str) -> str:
+    """The headline metric's name for a GEMM-family line: the contract's own
+    name for the fused forward at 32768 x 1024 x 4096, else the method and
+    the shape it was measured on."""
+    if variant == "fused" and (w.M, w.K, w.N) == (32768, 1024, 4096):
+        return METRIC
+    shape = "M%d K%d N%d" % (w.M, w.K, w.N) + ("" if variant == "lse" else " G%d" % w.G)
+    return "%s TFLOP/s at %s %s; %% MFMA peak" % (METHOD_NAMES[variant], shape, w.dtype)
+
+
 def headline_json(wl: Workload, rec: dict, args) -> dict:
     w = wl.w
     wall, kmean = rec["_wall"], rec["_kmean"]
@@ -700,7 +727,7 @@ def headline_json(wl: Workload, rec: dict, args) -> dict:
         cfg.update(M=w.M, K=w.K, N=w.N, G=w.G,
                    inputs="x~%g*N(0,1); W,b_lin~U(+-1/sqrt(K)); b_add~0.02*N(0,1); "
                           "gamma~1+0.1*N(0,1); beta~0.1*N(0,1)" % w.x_scale)
-        metric = METRIC
+        metric = gemm_metric(w, rec["variant"])
         kernel = {"fused": "lgn_fused_kernel", "twopass": "gemm+epilogue",
                   "wide": "wide partial+norm", "lse": "lse partial+finish"}[rec["variant"]]
     return {"metric": metric, "value": round(w.flops / (ms * 1e-3) / 1e12, 3),

@@ -86,9 +86,11 @@ def test_cpu_baseline_covers_every_headline_variant(tmp_path):
 
 
 def test_fraction_at_the_measured_clock():
-    tel = {"samples": 3, "sclk_mhz": {"min": 1800.0, "median": 1800.0, "max": 1800.0}}
+    tel = {"samples": 12, "sclk_mhz": {"min": 1800.0, "median": 1800.0, "max": 1800.0}}
     # 900 of a 2500 peak quoted at 2400 MHz: at 1800 MHz the peak is 1875
     assert bench.frac_at_clock(900.0, 2500.0, tel) == 0.48
+    # too few readings to stand for the region
+    assert bench.frac_at_clock(900.0, 2500.0, dict(tel, samples=2)) is None
     assert bench.frac_at_clock(900.0, 2500.0, {"samples": 0}) is None
     assert bench.frac_at_clock(900.0, 2500.0, None) is None
 
@@ -110,3 +112,13 @@ def test_check_leg_splits_methods_sharing_a_workload(monkeypatch):
     bench.check_outputs(wl, recs)
     for r in recs:
         assert r["check"]["count_gt_tol"] == 0 and r["check"]["elements"] == r["_host"].size
+
+
+def test_metric_names_the_method_and_shape():
+    from gemm_activation_groupnorm_amd import inputs as I
+    head = I.get_workload("m32768_k1024_n4096_g64_f32")
+    assert bench.gemm_metric(head, "fused") == bench.METRIC
+    lse = [w for w in I.LSE_WORKLOADS if w.dtype == "f32"][0]
+    m = bench.gemm_metric(lse, "lse")
+    assert m.startswith("Linear->logsumexp") and "M1024 K8192 N8192" in m
+    assert "two-pass" in bench.gemm_metric(head, "twopass")
