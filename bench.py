@@ -251,10 +251,10 @@ class _Timed:
         duration from one HIP event pair on the launch stream around them.
         `warmup` untimed launches first; with min_warm_ms > 0 the warm-up goes
         on until that much GPU time has passed (the clocks ramp up under load
-        over tens of milliseconds).  Returns (wall, mean_ms, w0, t1): the
-        telemetry window [w0, t1] is the timed region plus up to the last
-        100 ms of warm-up (the same launches, clocks settled), since a short
-        timed region alone holds too few sysfs samples."""
+        over tens of milliseconds).  Returns (wall, mean_ms, t0, t1, w0):
+        [t0, t1] is the timed region, w0 the start of the warm-up's last
+        100 ms (the same launches), for telemetry when the timed region alone
+        holds too few sysfs samples."""
         import torch
         t_warm = time.perf_counter()
         for _ in range(warmup):
@@ -273,7 +273,7 @@ class _Timed:
         end.record(self.stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        return t1 - t0, start.elapsed_time(end) / steps, max(t_warm, t0 - 0.1), t1
+        return t1 - t0, start.elapsed_time(end) / steps, t0, t1, max(t_warm, t0 - 0.1)
 
     def distribution(self, launches: int = 50, flush_bytes: int = 0):
         """Per-launch durations (one HIP event pair around each launch on the
@@ -474,9 +474,11 @@ def measure(wl: Workload, variant: str, steps: int, warmup: int, tel: Telemetry,
     """Times one entry point on one workload; returns its record (with the
     output kept on the host for the oracle leg under "_host")."""
     r = wl.runner(variant)
-    wall, kmean, t0, t1 = r.time(steps, warmup, min_warm_ms)
+    wall, kmean, t0, t1, w0 = r.time(steps, warmup, min_warm_ms)
     key = "%s/%s" % (wl.name, variant)
     tel.window(key, t0, t1)
+    if (tel.summary(key) or {}).get("samples", 0) < MIN_CLOCK_SAMPLES:
+        tel.window(key, w0, t1)
     rec = {"workload": wl.name, "variant": variant, "dtype": wl.dtype,
            "ms_per_step": round(wall / steps * 1e3, 4), "kernel_ms_mean": round(kmean, 4),
            "_wall": wall, "_kmean": kmean}
