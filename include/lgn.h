@@ -1,7 +1,9 @@
 /*
  * lgn.h -- C ABI of liblgn.so: fused Linear -> Swish -> +bias -> GroupNorm
- * on AMD Instinct MI355X (gfx950), plus Linear -> logsumexp -> LeakyReLU x2 ->
- * GELU x2 and Swish -> spatial GroupNorm -> HardSwish (declared at the end).
+ * on AMD Instinct MI355X (gfx950), its two-pass and wide-group forms, plus
+ * Linear -> logsumexp -> LeakyReLU x2 -> GELU x2, Swish -> spatial GroupNorm
+ * -> HardSwish and LayerNorm -> GELU -> dilated Conv1d -> + input (declared
+ * further down).
  *
  * The operation (POPCORNBENCH transcript "Kimi-K2.6 l2_p37", problem
  * statement and the passages fixing the forward order):
@@ -18,15 +20,19 @@
  *
  * Ownership: every pointer is DEVICE memory owned by the caller, on the
  * device that is current when the call is made.  The library allocates and
- * frees nothing.  `out` must not overlap any input.  The two-pass workspace
+ * frees nothing (lgn_forward_wide_f32_noalloc uses a fixed array the library
+ * holds per device instead of a workspace; see there).  `out` must not overlap any input.  The two-pass workspace
  * may be the same buffer as `out` (it is then overwritten in place) but must
  * not overlap any input.
  *
  * Execution: every call enqueues its kernels on `stream` and returns without
  * waiting; results are visible after the caller synchronises the stream.
  * Calls keep no state between them except a per-device cache of the device
- * architecture, so concurrent calls on different streams are safe.  Output is
- * bitwise reproducible run to run (fixed reduction order, no atomics).
+ * architecture (and the no-allocation entry point's array), so concurrent
+ * calls on different streams are safe, except overlapping calls of
+ * lgn_forward_wide_f32_noalloc on one device.  Output is bitwise reproducible
+ * run to run: every reduction has a fixed order, and the only atomics publish
+ * partial statistics (Swish -> spatial GroupNorm), never accumulate.
  *
  * Errors: calls return an lgn_status.  Argument errors are detected before any
  * HIP call and nothing is launched.  Faults inside a kernel surface at the

@@ -457,3 +457,23 @@ def test_noalloc_unsupported_and_empty(arch_override):
     assert _call_noalloc(M=0, x=None, out=None) == lgn.LGN_OK
     arch_override("gfx942")
     assert _call_noalloc() == lgn.LGN_ERR_UNSUPPORTED
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/lgn.h from a plain C99 program linked against liblgn.so: the
+    host helpers and argument checks answer without a GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    pkg = os.path.dirname(lgn.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    cmd = [gcc, "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "c_abi_check.c"), "-L", pkg, "-llgn",
+           "-Wl,-rpath," + pkg, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
