@@ -147,6 +147,8 @@ ONEPASS_SHAPES = [
     (1, 8, 16384 * 9 + 3, 2),    # 37 chunks per group
     (2, 2048, 5, 2),             # 1024 channels per group (the 1024 coefficient table)
     (1, 16384, 2, 2),            # 8192 channels per group (the 8192 coefficient table)
+    (1, 1, 16384 * 256, 1),      # 256 chunks per group: the single pass's limit
+    (1, 2, 16384 * 128 - 1, 1),  # 256 chunks, the last one 16382 elements
 ]
 
 
