@@ -13,7 +13,9 @@ namespace lgn {
 // (LDS DMA ring) -- BS samples x BC channels, waves along samples x channels:
 //   CG <= 64  : 256 x 256, 2 x 4 waves of 128 x 64; bf16: ring of 4 with the
 //               mid-stage barrier schedule; fp32: ring of 3
-//   CG == 128 : fp32: 256 x 128, 4 x 1 waves of 64 x 128, ring of 3;
+//   CG == 128 : fp32: 128 x 256, 2 x 2 waves of 64 x 128, ring of 3 (4.01 ms
+//               against 4.71 ms on 256 x 128 tiles of 4 x 1 waves at 16384 x
+//               2048 x 8192, output bitwise the same);
 //               bf16: the CG <= 64 tile, 2 waves per group
 //   CG == 256 : fp32: 128 x 256, 2 x 2 waves of 64 x 128 (2 waves per group), ring of 3;
 //               bf16: the CG <= 64 tile, 4 waves per group
@@ -22,7 +24,9 @@ namespace lgn {
 //   CG == 1024:  64 x 1024, 1 x 8 waves of 64 x 128 (8 waves per group), ring of 2;
 //                fp32 with the simple schedule (fragments read right before their MFMAs)
 //                and bands of 16 sample tiles
-// and register-staged tiles for any other K.
+// and register-staged tiles for any other K.  (For fp32 inputs with CG >= 512
+// and K a positive multiple of 16, lgn_forward_f32 runs the two-kernel form
+// instead: see fused_f32_runs_two_kernels.)
 template <class DT, class Cfg, int CG, int RING>
 hipError_t launch_fused_cfg(const typename dt_traits<DT>::storage *x,
                             const typename dt_traits<DT>::storage *W, const float *b_lin,
@@ -72,7 +76,7 @@ hipError_t launch_fused(const typename dt_traits<DT>::storage *x,
     // bf16 keeps the 256 x 256 tile up to CG = 256 (groups then span 2 or 4
     // waves, merged through LDS); fp32 measured faster on the narrower tiles
     constexpr bool BF = std::is_same<DT, bf16_t>::value;
-    typedef typename std::conditional<BF, F64, TileCfg<DT, 256, 128, 4, 1, 64, 2>>::type F128;
+    typedef typename std::conditional<BF, F64, TileCfg<DT, 128, 256, 2, 2, 64>>::type F128;
     typedef typename std::conditional<BF, F64, TileCfg<DT, 128, 256, 2, 2, 64>>::type F256;
     constexpr int R128 = BF ? 4 : 3;
     typedef typename std::conditional<BF, TileCfg<DT, 128, 512, 2, 4, 64, 2>,

@@ -52,6 +52,17 @@ inline bool fused_cg_supported(int cg) {
            cg == 512 || cg == 1024;
 }
 
+// fp32 inputs with 512 or 1024 channels per group: the fused kernel's tile is
+// then at most 64 samples tall (a taller one's fp32 accumulators would not fit
+// a CU's register file), so it reads W again for every 64 rows.  Two kernels
+// in place on `out` -- the GEMM on the 256 x 256 tile writing z, then the
+// GroupNorm epilogue -- measured as fast or faster at every M (2048 to 16384)
+// and K (1024 to 4096) tried: 3-8 % for 512 channels, up to 7 % for 1024 when
+// K >= 2048.  The 256 x 256 tile needs K a multiple of its 16-element stage.
+inline bool fused_f32_runs_two_kernels(int K, int cg) {
+    return cg >= 512 && K >= 16 && K % 16 == 0;
+}
+
 hipError_t launch_fused_f32(const float *x, const float *W, const float *b_lin,
                             const float *b_add, const float *gamma, const float *beta, int M,
                             int K, int N, int G, float eps, float *out, hipStream_t stream);

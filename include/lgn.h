@@ -73,12 +73,20 @@ typedef uint16_t lgn_bf16;
  *   K % 4 == 0 (fp32 inputs) or K % 8 == 0 (bf16 inputs); otherwise
  *   LGN_ERR_UNSUPPORTED.  b_lin, b_add, gamma, beta need 4-byte alignment. */
 
-/* Fused single-kernel forward, fp32 x and W, fp32 MFMA with fp32 accumulate.
+/* Fused forward, fp32 x and W, fp32 MFMA with fp32 accumulate.
  * One kernel: MFMA GEMM tile, then bias, Swish, bias, group statistics,
  * normalisation and affine in registers, and one write of `out`.
  * Covers channel-per-group counts C = N/G that are powers of two from 8 to
  * 1024; other C return LGN_ERR_UNSUPPORTED (the two-pass entry point covers
- * every C). */
+ * every C).
+ * Exception, for speed: with C = 512 or 1024 and K a positive multiple of 16,
+ * the call runs two kernels in place on `out` instead (the GEMM writes
+ * x W^T + b_lin into `out`, then one pass applies Swish, b_add, the group
+ * statistics and the affine).  A single-kernel tile holding whole groups that
+ * wide can be at most 64 samples tall -- a taller one's fp32 accumulators
+ * would not fit a compute unit's registers -- so it reads W again for every
+ * 64 rows, and the two kernels measured as fast or faster at every shape
+ * tried.  The result is the same up to rounding; `out` is written twice. */
 lgn_status lgn_forward_f32(const float *x, const float *W,
                            const float *b_lin, const float *b_add,
                            const float *gamma, const float *beta,
