@@ -66,6 +66,11 @@ SHAPES = [
     (300, 320, 768, 3),     # 256, 10 bf16 stages (bf16: 4 waves per group), ragged M
     (130, 64, 1024, 2),     # 512, 2 bf16 stages on the 128 x 512 bf16 tile, ragged M
     (200, 96, 2048, 2),     # 1024, 3 bf16 stages, ragged M over 64-sample tiles
+    # fp32 with 512 or 1024 channels per group runs two kernels when K % 16 == 0
+    # (K = 16: a single stage), the single register-staged kernel otherwise
+    (20, 16, 2048, 2),      # 1024, K = 16
+    (45, 24, 1024, 2),      # 512, K % 16 != 0: the single kernel
+    (37, 40, 2048, 2),      # 1024, K % 16 != 0: the single kernel
 ]
 
 
