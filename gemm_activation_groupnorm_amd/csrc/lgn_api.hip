@@ -301,7 +301,9 @@ lgn_status lgn_ln_gelu_conv1d_f32(const float *x, const float *ln_w, const float
         return LGN_ERR_INVALID_ARG;
     if (out == x) return LGN_ERR_INVALID_ARG;   // the convolution reads neighbours of x
     if (C % 128 != 0 || L % 4 != 0 || dilation > 16) return LGN_ERR_UNSUPPORTED;
-    if ((long long)C * L > 0x7fffffffLL) return LGN_ERR_UNSUPPORTED;
+    // the convolution addresses a sample and the packed weights with 32-bit
+    // byte offsets
+    if ((long long)C * L >= (1LL << 29) || C > 8192) return LGN_ERR_UNSUPPORTED;
     if (workspace_bytes < lgn_lnconv_workspace_bytes(B, C, L)) return LGN_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(ln_w, 16) || !aligned(ln_b, 16) || !aligned(out, 16) ||
         !aligned(workspace, 16) || !aligned(conv_w, 4) || !aligned(conv_b, 4))

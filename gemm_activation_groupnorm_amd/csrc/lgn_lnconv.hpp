@@ -154,27 +154,56 @@ __global__ __launch_bounds__(Tile::NT) void lgn_lnconv_kernel(
     f32x4 rw[WF4];
     f32x4 rx[GF4], rg[GF4], rb[GF4];
 
-    // global -> registers for stage s (input channels s*16 .. s*16+15)
+    // Buffer loads: per-thread byte offsets fixed for the whole loop, the
+    // stage's channel offset in a scalar register or in the descriptor's
+    // base.  A raw buffer (stride 0) returns 0 for an offset at or beyond its
+    // size, so the halo loads that fall outside the sample (the left halo of
+    // channel 0, the right halo of the last channel) read 0 and touch no
+    // memory.  0x00020000 is the gfx9 descriptor word for 32-bit data.  The
+    // API keeps C * L below 2^29 and C at most 8192, so every offset fits 31
+    // bits.
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc((void *)wt, (short)0, 3 * C * C * 4, 0x00020000);
+    int vo_w[WF4], vo_g[GF4];
+#pragma unroll
+    for (int q = 0; q < WF4; ++q) {
+        const int f = tid + q * NT;
+        const int row = f / (CO / 4), col4 = f % (CO / 4);
+        const int t = row / kLcKc, cl = row % kLcKc;
+        vo_w[q] = 4 * ((t * C + cl) * C + co0 + 4 * col4);
+    }
+#pragma unroll
+    for (int q = 0; q < GF4; ++q) {
+        const int f = tid + q * NT;
+        const int cl = f / win4, col4 = f - cl * win4;
+        vo_g[q] = 4 * (cl * L + j0 - H + 4 * col4);
+    }
     auto load_stage = [&](int s) {
         const int c0 = s * kLcKc;
 #pragma unroll
-        for (int q = 0; q < WF4; ++q) {
-            const int f = tid + q * NT;
-            const int row = f / (CO / 4), col4 = f % (CO / 4);   // row = t * 16 + cl
-            const int t = row / kLcKc, cl = row % kLcKc;
-            rw[q] = *reinterpret_cast<const f32x4 *>(
-                wt + ((size_t)(t * C + c0 + cl) * C + co0 + 4 * col4));
-        }
+        for (int q = 0; q < WF4; ++q)
+            rw[q] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, vo_w[q], 4 * c0 * C, 0));
+        // the activation buffers start at this stage's first channel and end
+        // at the sample's last one, so every halo load outside them reads 0
+        const size_t cs = (size_t)c0 * L;
+        const int rem = (C - c0) * L * 4;
+        const __amdgpu_buffer_rsrc_t rs_x =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(xb + cs), (short)0, rem, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs_g =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(ln_w + cs), (short)0, rem, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs_b =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(ln_b + cs), (short)0, rem, 0x00020000);
 #pragma unroll
         for (int q = 0; q < GF4; ++q) {
             const int f = tid + q * NT;
-            const int cl = f / win4, col4 = f - cl * win4;
-            const int p = j0 - H + 4 * col4;
-            if (f < gtot && p >= 0 && p < L) {
-                const size_t o = (size_t)(c0 + cl) * L + p;
-                rx[q] = *reinterpret_cast<const f32x4 *>(xb + o);
-                rg[q] = *reinterpret_cast<const f32x4 *>(ln_w + o);
-                rb[q] = *reinterpret_cast<const f32x4 *>(ln_b + o);
+            if (f < gtot) {
+                rx[q] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, vo_g[q], 0, 0));
+                rg[q] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, vo_g[q], 0, 0));
+                rb[q] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_b, vo_g[q], 0, 0));
             }
         }
     };

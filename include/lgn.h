@@ -211,8 +211,9 @@ lgn_status lgn_swish_gn_hardswish_f32(const float *y, const float *gamma, const 
  * `workspace` must hold lgn_lnconv_workspace_bytes(B, C, L) bytes, be 16-byte
  * aligned and overlap nothing else.  Rules: B >= 0 (0 is a no-op), C >= 1,
  * L >= 1, dilation >= 1, eps > 0 and finite, else LGN_ERR_INVALID_ARG;
- * C % 128, L % 4, dilation > 16, C*L > 2^31 - 1 or x, ln_w, ln_b, out not
- * 16-byte aligned give LGN_ERR_UNSUPPORTED.  Results are bitwise
+ * C % 128, L % 4, dilation > 16, C > 8192, C*L >= 2^29 (one sample and the
+ * packed weights are addressed with 32-bit byte offsets) or x, ln_w, ln_b,
+ * out not 16-byte aligned give LGN_ERR_UNSUPPORTED.  Results are bitwise
  * reproducible. */
 size_t lgn_lnconv_workspace_bytes(int B, int C, int L);
 

@@ -281,7 +281,8 @@ LNC_INVALID = [dict(B=-1), dict(C=0), dict(L=0), dict(d=0), dict(eps=0.0), dict(
                dict(ws_bytes=lgn.lgn_lnconv_workspace_bytes(2, 256, 4096) - 1)]
 LNC_UNSUPPORTED = [dict(C=192), dict(L=4094), dict(d=17), dict(x=A + 4), dict(ln_w=A + 8),
                    dict(ln_b=A + 4), dict(out=A + 4100), dict(ws=A + 8), dict(conv_w=A + 2),
-                   dict(C=1 << 16, L=1 << 16)]
+                   dict(C=1 << 16, L=1 << 16), dict(C=1 << 14, L=1 << 15),
+                   dict(C=8320, L=4)]
 
 
 @pytest.mark.parametrize("bad", LNC_INVALID, ids=lambda d: ",".join("%s=%s" % i for i in d.items()))
