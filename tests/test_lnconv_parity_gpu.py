@@ -41,6 +41,8 @@ SHAPES = [
     (1, 384, 64, 1, True),       # dilation 1, three channel tiles
     (2, 128, 4, 2, False),       # a single float4 of positions
     (1, 256, 256, 5, False),     # dilation 5 (halo 8); 64K values = four stats chunks
+    (1, 8192, 64, 16, False),    # the largest C: 805 MB of packed weights, 32-bit offsets
+                                 # near their bound; the position tile larger than L
 ]
 
 
