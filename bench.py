@@ -692,10 +692,14 @@ METHOD_NAMES = {
 
 
 def fused_runs_two_kernels(w) -> bool:
-    """lgn_forward_f32's own dispatch (include/lgn.h): fp32 inputs, 512 or
-    more channels per group and K a positive multiple of 16 run the GEMM and
-    the GroupNorm epilogue as two kernels."""
-    return w.dtype == "f32" and w.N // w.G >= 512 and w.K >= 16 and w.K % 16 == 0
+    """The fused entry points' own dispatch (include/lgn.h): fp32 inputs with
+    512 or more channels per group and K a positive multiple of 16, or bf16
+    inputs with 1024 channels per group and K >= 2048 a multiple of 32, run
+    the GEMM and the GroupNorm epilogue as two kernels."""
+    c = w.N // w.G
+    if w.dtype == "f32":
+        return c >= 512 and w.K >= 16 and w.K % 16 == 0
+    return c == 1024 and w.K >= 2048 and w.K % 32 == 0
 
 
 def gemm_metric(w, variant: str) -> str:
@@ -743,7 +747,7 @@ def headline_json(wl: Workload, rec: dict, args) -> dict:
         kernel = {"fused": "lgn_fused_kernel", "twopass": "gemm+epilogue",
                   "wide": "wide partial+norm", "lse": "lse partial+finish"}[rec["variant"]]
         if rec["variant"] == "fused" and fused_runs_two_kernels(w):
-            kernel = "gemm+epilogue (lgn_forward_f32 at %d channels per group)" % (w.N // w.G)
+            kernel = "gemm+epilogue (fused entry point at %d channels per group)" % (w.N // w.G)
     return {"metric": metric, "value": round(w.flops / (ms * 1e-3) / 1e12, 3),
             "unit": "TFLOP/s", **base, "config": cfg,
             "roofline": {"bound": "mfma", "achieved": round(ach, 3), "peak": peak,

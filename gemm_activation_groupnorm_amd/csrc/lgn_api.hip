@@ -85,11 +85,15 @@ lgn_status forward_fused(const T *x, const T *W, const float *b_lin, const float
     if (!lgn::fused_cg_supported(N / G)) return LGN_ERR_UNSUPPORTED;
     s = check_device();
     if (s != LGN_OK) return s;
-    if (DT == DT_F32 && lgn::fused_f32_runs_two_kernels(K, N / G)) {
+    if (DT == DT_F32 ? lgn::fused_f32_runs_two_kernels(K, N / G)
+                     : lgn::fused_bf16_runs_two_kernels(K, N / G)) {
         // z = x W^T + b_lin into out on the 256 x 256 GEMM tile, then the
         // GroupNorm epilogue in place
-        hipError_t e = lgn::launch_gemm_bias_f32((const float *)x, (const float *)W, b_lin, M, K,
-                                                 N, out, stream);
+        hipError_t e = DT == DT_F32
+                           ? lgn::launch_gemm_bias_f32((const float *)x, (const float *)W, b_lin,
+                                                       M, K, N, out, stream)
+                           : lgn::launch_gemm_bias_bf16((const uint16_t *)x, (const uint16_t *)W,
+                                                        b_lin, M, K, N, out, stream);
         if (e != hipSuccess) return from_hip(e);
         return from_hip(lgn::launch_gn_epilogue(out, b_add, gamma, beta, M, N, G, eps, out,
                                                 stream));

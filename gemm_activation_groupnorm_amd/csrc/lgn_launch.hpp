@@ -62,6 +62,13 @@ inline bool fused_cg_supported(int cg) {
 inline bool fused_f32_runs_two_kernels(int K, int cg) {
     return cg >= 512 && K >= 16 && K % 16 == 0;
 }
+// bf16 inputs: the single kernel wins at K = 1024 (by up to 19 %), the two
+// kernels at 1024 channels per group once K >= 2048 (3-22 % at M = 2048 to
+// 16384); 512-channel groups are mixed and keep the single kernel.  The bf16
+// 256 x 256 tile's stage is 32 elements.
+inline bool fused_bf16_runs_two_kernels(int K, int cg) {
+    return cg == 1024 && K >= 2048 && K % 32 == 0;
+}
 
 hipError_t launch_fused_f32(const float *x, const float *W, const float *b_lin,
                             const float *b_add, const float *gamma, const float *beta, int M,

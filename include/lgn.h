@@ -94,7 +94,9 @@ lgn_status lgn_forward_f32(const float *x, const float *W,
                            float *out, hipStream_t stream);
 
 /* Same as lgn_forward_f32 with x and W in bfloat16 (bf16 MFMA, fp32
- * accumulate); biases, gamma, beta and out stay fp32. */
+ * accumulate); biases, gamma, beta and out stay fp32.  The two-kernel
+ * exception applies here to C = 1024 with K >= 2048 and a multiple of 32
+ * only: for bf16 the single kernel is faster at smaller K and at C = 512. */
 lgn_status lgn_forward_bf16(const lgn_bf16 *x, const lgn_bf16 *W,
                             const float *b_lin, const float *b_add,
                             const float *gamma, const float *beta,

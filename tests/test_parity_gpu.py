@@ -71,6 +71,7 @@ SHAPES = [
     (20, 16, 2048, 2),      # 1024, K = 16
     (45, 24, 1024, 2),      # 512, K % 16 != 0: the single kernel
     (37, 40, 2048, 2),      # 1024, K % 16 != 0: the single kernel
+    (70, 2048, 2048, 2),    # 1024, K = 2048: two kernels for bf16 too
 ]
 
 
