@@ -54,10 +54,10 @@ template <int LPG, int V>
 static hipError_t launch_vec(const float *z, const float *b_add, const float *gamma,
                              const float *beta, long long pairs, int G, float eps, float *out,
                              hipStream_t stream) {
-    constexpr long long per_block = 4 * (64 / LPG);
+    constexpr long long per_block = 64 / LPG;   // one wave per workgroup
     const long long blocks = (pairs + per_block - 1) / per_block;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    return launch_kernel(lgn_gn_epilogue_vec_kernel<LPG, V>, dim3((unsigned)blocks), dim3(256),
+    return launch_kernel(lgn_gn_epilogue_vec_kernel<LPG, V>, dim3((unsigned)blocks), dim3(64),
                          stream, z, b_add, gamma, beta, pairs, G, eps, out);
 }
 
@@ -77,11 +77,9 @@ hipError_t launch_gn_epilogue(const float *z, const float *b_add, const float *g
         case 512: return launch_vec<64, 2>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
         case 1024: return launch_vec<64, 4>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
         default: {
-            const long long blocks = (pairs + 3) / 4;
-            if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-            return launch_kernel(lgn_gn_epilogue_generic_kernel, dim3((unsigned)blocks),
-                                 dim3(256), stream, z, b_add, gamma, beta, pairs, G, cg, eps,
-                                 out);
+            if (pairs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+            return launch_kernel(lgn_gn_epilogue_generic_kernel, dim3((unsigned)pairs), dim3(64),
+                                 stream, z, b_add, gamma, beta, pairs, G, cg, eps, out);
         }
     }
 }

@@ -90,16 +90,17 @@ void lgn_gemm_bias_kernel(
 // Statistics: per-lane local two-pass, then an xor-butterfly of equal-count
 // Chan merges inside each LPG-lane segment.  In place (out == z) is safe:
 // every value is read before the pair's outputs are written, by the same
-// lane.
+// lane.  One wave per workgroup: more, smaller workgroups keep more of the
+// HBM stream in flight (3-17 % faster than four waves per workgroup across
+// 64- to 1024-channel groups at 16384 x 8192, bitwise the same output).
 template <int LPG, int V>
-__global__ __launch_bounds__(256) void lgn_gn_epilogue_vec_kernel(
+__global__ __launch_bounds__(64) void lgn_gn_epilogue_vec_kernel(
     const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
     const float *__restrict__ beta, long long pairs, int G, float eps, float *out) {
     constexpr int CG = 4 * LPG * V;
     constexpr int PPW = 64 / LPG;   // pairs per wave
     const int lane = threadIdx.x & 63;
-    const long long wave_global = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const long long p = wave_global * PPW + lane / LPG;
+    const long long p = (long long)blockIdx.x * PPW + lane / LPG;
     const int j = lane % LPG;
     const bool live = p < pairs;
     const int g = live ? (int)(p % G) : 0;
@@ -158,12 +159,11 @@ __global__ __launch_bounds__(256) void lgn_gn_epilogue_vec_kernel(
 // Epilogue, any channel count: one wave per (row, group), three passes over
 // the group (sum; sum of squared deviations from the mean; normalise), each
 // an xor-butterfly sum over the wave.  Used when C is not 4*LPG*V.
-__global__ __launch_bounds__(256) void lgn_gn_epilogue_generic_kernel(
+__global__ __launch_bounds__(64) void lgn_gn_epilogue_generic_kernel(
     const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
     const float *__restrict__ beta, long long pairs, int G, int CG, float eps, float *out) {
     const int lane = threadIdx.x & 63;
-    const long long p = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (p >= pairs) return;   // whole wave leaves together
+    const long long p = blockIdx.x;
     const int g = (int)(p % G);
     const size_t base = (size_t)p * CG;
     float sum = 0.f;
