@@ -233,13 +233,15 @@ MIN_CLOCK_SAMPLES = 5
 
 def frac_at_clock(achieved: float, peak: float, telemetry) -> Optional[float]:
     """achieved / (peak scaled to the median shader clock of the timed
-    region), or None without at least MIN_CLOCK_SAMPLES clock readings."""
+    region), or None without at least MIN_CLOCK_SAMPLES clock readings or
+    while the readings still move by more than 10 % (the sysfs clock level
+    trails a GPU that has just left idle)."""
     try:
-        mhz = telemetry["sclk_mhz"]["median"]
-        n = telemetry["samples"]
+        clk = telemetry["sclk_mhz"]
+        mhz, n = clk["median"], telemetry["samples"]
     except (TypeError, KeyError):
         return None
-    if not mhz or n < MIN_CLOCK_SAMPLES:
+    if not mhz or n < MIN_CLOCK_SAMPLES or (clk["max"] - clk["min"]) > 0.1 * mhz:
         return None
     return round(achieved / (peak * mhz / PEAK_SCLK_MHZ), 4)
 

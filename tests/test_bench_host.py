@@ -91,6 +91,9 @@ def test_fraction_at_the_measured_clock():
     assert bench.frac_at_clock(900.0, 2500.0, tel) == 0.48
     # too few readings to stand for the region
     assert bench.frac_at_clock(900.0, 2500.0, dict(tel, samples=2)) is None
+    # readings still ramping up from idle
+    ramp = {"samples": 9, "sclk_mhz": {"min": 1053.0, "median": 1516.0, "max": 1820.0}}
+    assert bench.frac_at_clock(140.0, 157.3, ramp) is None
     assert bench.frac_at_clock(900.0, 2500.0, {"samples": 0}) is None
     assert bench.frac_at_clock(900.0, 2500.0, None) is None
 
