@@ -581,6 +581,31 @@ def _check_group(wl: Workload, recs: list) -> None:
         eprint("[bench] check %s/%s: max abs %.3e, mean abs %.3e, %d of %d > %.0e (%.1f s)"
                % (wl.name, r["variant"], st.max, r["check"]["mean_abs_err"], st.over, st.n,
                   st.tol, time.perf_counter() - t0))
+    if wl.kind == "gemm" and wl.dtype == "bf16" and recs[0]["variant"] != "lse":
+        _check_against_unrounded_inputs(wl, recs)
+
+
+def _check_against_unrounded_inputs(wl: Workload, recs: list) -> None:
+    """For information only (the gate is the oracle on the bf16 values the
+    GPU reads): the error against the oracle on the fp32 draws before their
+    rounding to bf16, i.e. what the bf16 input costs."""
+    import oracle
+    from gemm_activation_groupnorm_amd import inputs as I
+    w = wl.w
+    f = I.make_inputs(w.M, w.K, w.N, w.seed, "f32", w.x_scale)
+    stats = [ErrStats(TOL["bf16"]) for _ in recs]
+    for a in range(0, w.M, 2048):
+        b = min(w.M, a + 2048)
+        ref = oracle.lgn_forward(f["x"][a:b], f["W"], f["b_lin"], f["b_add"], f["gamma"],
+                                 f["beta"], w.G, w.eps)
+        for st, r in zip(stats, recs):
+            st.add(r["_host"][a:b], ref)
+    for st, r in zip(stats, recs):
+        info = st.summary()
+        info["vs"] = "fp64 oracle on the fp32 inputs before bf16 rounding (information, not a gate)"
+        r["check_vs_unrounded_inputs"] = info
+        eprint("[bench] %s/%s against the unrounded fp32 inputs: max abs %.3e, mean abs %.3e"
+               % (wl.name, r["variant"], st.max, info["mean_abs_err"]))
 
 
 def cpu_baseline(wl: Workload, variant: str, seconds: float, tmpdir: str) -> dict:
@@ -857,6 +882,8 @@ def main():
         for wl, recs in measured:
             check_outputs(wl, recs)
         res["check"] = head_rec["check"]
+        if "check_vs_unrounded_inputs" in head_rec:
+            res["check_vs_unrounded_inputs"] = head_rec["check_vs_unrounded_inputs"]
         with tempfile.TemporaryDirectory() as td:
             res["cpu_baseline"] = cpu_baseline(head_wl, head_rec["variant"], args.cpu_seconds, td)
             eprint("[bench] cpu baseline: %s" % res["cpu_baseline"]["sample"])

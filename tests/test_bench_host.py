@@ -125,3 +125,23 @@ def test_metric_names_the_method_and_shape():
     m = bench.gemm_metric(lse, "lse")
     assert m.startswith("Linear->logsumexp") and "M1024 K8192 N8192" in m
     assert "two-pass" in bench.gemm_metric(head, "twopass")
+
+
+def test_bf16_lines_also_report_the_unrounded_input_error():
+    """The bf16 gate is the oracle on the bf16 values; the error against the
+    fp32 draws before rounding is reported beside it as information."""
+    import types
+    from gemm_activation_groupnorm_amd import inputs as I
+    import oracle
+    w = I.Workload("tiny_bf16", 64, 32, 128, 8, "bf16", 3)
+    inp = I.workload_inputs(w)
+    wl = types.SimpleNamespace(kind="gemm", w=w, inp=inp, name=w.name, dtype="bf16")
+    y = oracle.lgn_forward(inp["x"], inp["W"], inp["b_lin"], inp["b_add"], inp["gamma"],
+                           inp["beta"], w.G, w.eps).astype(np.float32)
+    recs = [{"variant": "fused", "_host": y}]
+    bench.check_outputs(wl, recs)
+    r = recs[0]
+    assert r["check"]["max_abs_err"] < 1e-5          # exact oracle on the bf16 values
+    info = r["check_vs_unrounded_inputs"]
+    assert "not a gate" in info["vs"] and info["elements"] == y.size
+    assert info["max_abs_err"] > r["check"]["max_abs_err"]   # the rounding shows
