@@ -186,3 +186,34 @@ def test_sgh_groups_beyond_the_single_pass_take_two_kernels():
     err = _err(out.cpu().numpy(), ref)
     log("  max abs err %.3e" % err)
     assert err <= TOL["f32"]
+
+
+def test_sgh_single_pass_calls_overlapping_on_two_streams():
+    # Two single-pass calls in flight at once, each with its own workspace.
+    # They share the GPU, so a group's chunks need not all be resident at the
+    # same time; a wait that runs out falls back to forming the statistics
+    # from y.  Either way each output must be bitwise that of the same call
+    # made alone.
+    shapes = [(8, 16, 31 * 63 * 9, 4), (6, 8, 16384 * 20 + 5, 2)]
+    calls = []
+    for k, (Nb, C, S, G) in enumerate(shapes):
+        inp = make_sgh_inputs(Nb, C, S, 950 + k)
+        d = dev(inp)
+        nb = lgn.lgn_sgh_workspace_bytes(Nb, C, S, G)
+        ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device="cuda")
+        alone = torch.empty((Nb, C, S), dtype=torch.float32, device="cuda")
+        both = torch.full((Nb, C, S), float("nan"), dtype=torch.float32, device="cuda")
+        calls.append((d, Nb, C, S, G, nb, ws, alone, both))
+    log("sgh single pass alone, then two streams at once: %s" % (shapes,))
+    for d, Nb, C, S, G, nb, ws, alone, both in calls:
+        lgn.check(lgn.lgn_swish_gn_hardswish_f32(d["y"], d["gamma"], d["beta"], Nb, C, S, G,
+                                                 1e-5, alone, ws, nb))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        for st, (d, Nb, C, S, G, nb, ws, alone, both) in zip(streams, calls):
+            lgn.check(lgn.lgn_swish_gn_hardswish_f32(d["y"], d["gamma"], d["beta"], Nb, C, S, G,
+                                                     1e-5, both, ws, nb, stream=st))
+    torch.cuda.synchronize()
+    for d, Nb, C, S, G, nb, ws, alone, both in calls:
+        assert torch.equal(alone, both)
