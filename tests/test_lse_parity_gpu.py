@@ -66,11 +66,13 @@ def test_lse_shapes(shape, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shift", [-12.0, 6.0])
+@pytest.mark.parametrize("shift", [-200.0, -12.0, 6.0, 200.0])
 def test_lse_activation_branches(shift, dtype):
     # a bias far below 0 makes every logsumexp negative (both LeakyReLUs then
     # scale it by 0.01 and the GELUs see small negative values); far above,
-    # the activations are close to the identity
+    # the activations are close to the identity.  At +-200 every exp of an
+    # unshifted z overflows (or underflows) in fp32: only the max-shifted
+    # partials and their merge keep the result finite and exact
     M, K, N = 96, 64, 512
     inp = make_inputs(M, K, N, 77, dtype)
     inp["b_lin"] = (inp["b_lin"] + np.float32(shift)).astype(np.float32)
