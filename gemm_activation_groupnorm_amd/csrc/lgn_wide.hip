@@ -78,10 +78,12 @@ hipError_t launch_wide(const typename dt_traits<DT>::storage *x,
                           part);
     }
     if (e != hipSuccess) return e;
-    const long long pairs = (long long)M * G;
-    return launch_kernel(lgn_wide_norm_kernel<kWideSpan>, dim3((unsigned)((pairs + 3) / 4)),
-                         dim3(256), stream, (const float2 *)part, gamma, beta, pairs, G,
-                         (N / G) / kWideSpan, N / kWideSpan, eps, out);
+    // one wave per (pair of rows, group)
+    const long long waves = ((long long)M + kWideNormRows - 1) / kWideNormRows * G;
+    if (waves > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    return launch_kernel(lgn_wide_norm_kernel<kWideSpan>, dim3((unsigned)waves), dim3(64), stream,
+                         (const float2 *)part, gamma, beta, (long long)M, G, (N / G) / kWideSpan,
+                         N / kWideSpan, eps, out);
 }
 
 hipError_t launch_wide_f32(const float *x, const float *W, const float *b_lin, const float *b_add,

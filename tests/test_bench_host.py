@@ -145,3 +145,16 @@ def test_bf16_lines_also_report_the_unrounded_input_error():
     info = r["check_vs_unrounded_inputs"]
     assert "not a gate" in info["vs"] and info["elements"] == y.size
     assert info["max_abs_err"] > r["check"]["max_abs_err"]   # the rounding shows
+
+
+def test_headline_workload_defaults_per_variant():
+    import bench
+    d = bench.DEFAULT_WORKLOAD
+    assert bench.headline_workload(d, "fused") == d
+    assert bench.headline_workload(d, "twopass") == d
+    assert bench.headline_workload(d, "wide") == "m16384_k2048_n8192_g8_f32"
+    assert bench.headline_workload(d, "lse") == "m1024_k8192_n8192_lse_f32"
+    assert bench.headline_workload(d, "sgh") == "n128_c16_d31_h63_w63_g4_sgh_f32"
+    assert bench.headline_workload(d, "lnconv") == "b32_c256_l4096_d4_lnconv_f32"
+    # an explicit workload is kept
+    assert bench.headline_workload("m16384_k2048_n8192_g1_f32", "wide") == "m16384_k2048_n8192_g1_f32"

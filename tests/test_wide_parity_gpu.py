@@ -74,3 +74,25 @@ def test_wide_deterministic_and_row_split():
     torch.cuda.synchronize()
     assert torch.equal(y1, y2), "run-to-run difference"
     assert torch.equal(torch.cat([ya, yb]), y1), "row split changes results"
+
+
+@pytest.mark.parametrize("M", [131, 132])
+def test_wide_no_writes_outside_output_or_workspace(M):
+    # The normalise kernel takes rows in pairs: with an odd M the last pair
+    # has one row, and nothing past row M-1 may be written.
+    K, N, G = 64, 512, 2
+    log("wide bounds case M=%d K=%d N=%d G=%d" % (M, K, N, G))
+    inp = case(M, K, N, G, 45)
+    dev = to_device(inp, "f32")
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
+    nb = lgn.lgn_wide_workspace_bytes(M, N)
+    wsbuf = torch.full((nb // 4 + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
+    lgn.check(lgn.lgn_forward_wide_f32(dev["x"], dev["W"], dev["b_lin"], dev["b_add"],
+                                       dev["gamma"], dev["beta"], M, K, N, G, 1e-5,
+                                       buf.data_ptr() + pad * 4, wsbuf.data_ptr() + pad * 4, nb))
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == 12345.0).all()) and bool((buf[pad + M * N:] == 12345.0).all())
+    assert bool((wsbuf[:pad] == 12345.0).all()) and bool((wsbuf[pad + nb // 4:] == 12345.0).all())
+    y = buf[pad:pad + M * N].view(M, N).cpu().numpy()
+    assert max_err(y, oracle_rows(inp, G, 1e-5)) <= TOL["f32"]
