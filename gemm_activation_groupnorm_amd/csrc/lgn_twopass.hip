@@ -52,13 +52,15 @@ hipError_t launch_gemm_bias_bf16(const uint16_t *x, const uint16_t *W, const flo
 
 template <int LPG, int V>
 static hipError_t launch_vec(const float *z, const float *b_add, const float *gamma,
-                             const float *beta, long long pairs, int G, float eps, float *out,
+                             const float *beta, int M, int G, float eps, float *out,
                              hipStream_t stream) {
-    constexpr long long per_block = 64 / LPG;   // one wave per workgroup
-    const long long blocks = (pairs + per_block - 1) / per_block;
+    // one wave per workgroup, 64/LPG units (row pair, group) per wave
+    constexpr long long per_block = 64 / LPG;
+    const long long units = ((long long)M + 1) / 2 * G;
+    const long long blocks = (units + per_block - 1) / per_block;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     return launch_kernel(lgn_gn_epilogue_vec_kernel<LPG, V>, dim3((unsigned)blocks), dim3(64),
-                         stream, z, b_add, gamma, beta, pairs, G, eps, out);
+                         stream, z, b_add, gamma, beta, (long long)M, G, eps, out);
 }
 
 hipError_t launch_gn_epilogue(const float *z, const float *b_add, const float *gamma,
@@ -67,15 +69,15 @@ hipError_t launch_gn_epilogue(const float *z, const float *b_add, const float *g
     const int cg = N / G;
     const long long pairs = (long long)M * G;
     switch (cg) {
-        case 4: return launch_vec<1, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
-        case 8: return launch_vec<2, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
-        case 16: return launch_vec<4, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
-        case 32: return launch_vec<8, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
-        case 64: return launch_vec<16, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
-        case 128: return launch_vec<32, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
-        case 256: return launch_vec<64, 1>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
-        case 512: return launch_vec<64, 2>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
-        case 1024: return launch_vec<64, 4>(z, b_add, gamma, beta, pairs, G, eps, out, stream);
+        case 4: return launch_vec<1, 1>(z, b_add, gamma, beta, M, G, eps, out, stream);
+        case 8: return launch_vec<2, 1>(z, b_add, gamma, beta, M, G, eps, out, stream);
+        case 16: return launch_vec<4, 1>(z, b_add, gamma, beta, M, G, eps, out, stream);
+        case 32: return launch_vec<8, 1>(z, b_add, gamma, beta, M, G, eps, out, stream);
+        case 64: return launch_vec<16, 1>(z, b_add, gamma, beta, M, G, eps, out, stream);
+        case 128: return launch_vec<32, 1>(z, b_add, gamma, beta, M, G, eps, out, stream);
+        case 256: return launch_vec<64, 1>(z, b_add, gamma, beta, M, G, eps, out, stream);
+        case 512: return launch_vec<64, 2>(z, b_add, gamma, beta, M, G, eps, out, stream);
+        case 1024: return launch_vec<64, 4>(z, b_add, gamma, beta, M, G, eps, out, stream);
         default: {
             if (pairs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
             return launch_kernel(lgn_gn_epilogue_generic_kernel, dim3((unsigned)pairs), dim3(64),
