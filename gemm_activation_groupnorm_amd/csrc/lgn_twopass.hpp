@@ -178,9 +178,129 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_vec_kernel(
     }
 }
 
+// Epilogue for a group width CG that is a multiple of 4 but not of the form
+// 4*LPG*V: the vectorised kernel's layout with the slots past the group's
+// F = CG/4 float4s masked off (LPG >= F when V == 1, else LPG = 64 and
+// 64*V >= F), for R rows per lane: unit q = (block of R rows, group g),
+// q = rb*G + g, one load of b_add, gamma and beta serving the R rows.  A
+// lane's count of values varies (0 for a lane with no slot), so the merges
+// across the LPG lanes carry counts: Chan's update, lower lane first, so both
+// lanes of a pair hold the same bits.
+template <int LPG, int V, int R>
+__global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
+    const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
+    const float *__restrict__ beta, long long M, int G, int CG, float eps, float *out) {
+    constexpr int UPW = 64 / LPG;   // units per wave
+    const int lane = threadIdx.x & 63;
+    const long long units = (M + R - 1) / R * G;
+    const long long q = (long long)blockIdx.x * UPW + lane / LPG;
+    const int j = lane % LPG;
+    const bool live = q < units;
+    const long long r0 = live ? (long long)R * (q / G) : 0;
+    const int g = live ? (int)(q % G) : 0;
+    const int F = CG / 4;
+    size_t base[R];
+    bool valid[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        valid[r] = live && r0 + r < M;
+        base[r] = ((size_t)(valid[r] ? r0 + r : r0) * G + g) * CG;   // a missing row reads row r0
+    }
+
+    f32x4 u[R][V];
+    float sum[R], n = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) sum[r] = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int f = j + LPG * v;
+        const bool in = live && f < F;
+        f32x4 ba = {0.f, 0.f, 0.f, 0.f};
+        if (in) {
+            const int ch = g * CG + 4 * f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ba[e] = b_add[ch + e];
+            n += 4.f;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            f32x4 val = {0.f, 0.f, 0.f, 0.f};
+            if (in) {
+                val = *reinterpret_cast<const f32x4 *>(z + base[r] + 4 * f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = swish(val[e]) + ba[e];
+            }
+            u[r][v] = val;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[r] += val[e];
+        }
+    }
+    float mean[R], rstd[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float mn = n > 0.f ? sum[r] / n : 0.f;
+        float m2 = 0.f, cnt = n;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (j + LPG * v < F) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float d = u[r][v][e] - mn;
+                    m2 += d * d;
+                }
+            }
+#pragma unroll
+        for (int off = 1; off < LPG; off <<= 1) {
+            const float om = __shfl_xor(mn, off), om2 = __shfl_xor(m2, off),
+                        on = __shfl_xor(cnt, off);
+            const bool lower = (lane & off) == 0;
+            const float am = lower ? mn : om, am2 = lower ? m2 : om2, an = lower ? cnt : on;
+            const float bm = lower ? om : mn, bm2 = lower ? om2 : m2, bn = lower ? on : cnt;
+            const float nt = an + bn;
+            if (bn == 0.f) {
+                mn = am;
+                m2 = am2;
+            } else if (an == 0.f) {
+                mn = bm;
+                m2 = bm2;
+            } else {
+                const float d = bm - am;
+                const float fr = bn / nt;
+                mn = am + d * fr;
+                m2 = am2 + bm2 + d * d * (an * fr);
+            }
+            cnt = nt;
+        }
+        mean[r] = mn;
+        rstd[r] = __builtin_amdgcn_rsqf(m2 / (float)CG + eps);
+    }
+    if (!live) return;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int f = j + LPG * v;
+        if (f < F) {
+            const int ch = g * CG + 4 * f;
+            float ga[4], be[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ga[e] = gamma[ch + e];
+                be[e] = beta[ch + e];
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = (u[r][v][e] - mean[r]) * rstd[r] * ga[e] + be[e];
+                if (valid[r]) *reinterpret_cast<f32x4 *>(out + base[r] + 4 * f) = y;
+            }
+        }
+    }
+}
+
 // Epilogue, any channel count: one wave per (row, group), three passes over
 // the group (sum; sum of squared deviations from the mean; normalise), each
-// an xor-butterfly sum over the wave.  Used when C is not 4*LPG*V.
+// an xor-butterfly sum over the wave.  Used when C is not a multiple of 4 or
+// is above 4096.
 __global__ __launch_bounds__(64) void lgn_gn_epilogue_generic_kernel(
     const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
     const float *__restrict__ beta, long long pairs, int G, int CG, float eps, float *out) {

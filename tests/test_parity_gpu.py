@@ -87,7 +87,13 @@ def test_shapes(shape, dtype, variant):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(50, 32, 96, 8), (37, 16, 12, 4), (20, 24, 8, 4),
-                                   (9, 32, 2048, 1), (12, 40, 1200, 10)],
+                                   (9, 32, 2048, 1), (12, 40, 1200, 10),
+                                   # C a multiple of 4 but not a power of two: 48, 96, 200,
+                                   # 768 (three float4s per lane, one slot masked), 4096;
+                                   # then 6144 and 50, which take the generic kernel
+                                   (33, 32, 480, 10), (29, 24, 768, 8), (17, 40, 4000, 20),
+                                   (13, 16, 3072, 4), (7, 32, 4096, 1), (5, 8, 12288, 2),
+                                   (21, 16, 100, 2)],
                          ids=lambda s: "M%d_K%d_N%d_G%d" % s)
 def test_twopass_other_group_widths(shape, dtype):
     M, K, N, G = shape
@@ -234,6 +240,26 @@ def test_no_writes_outside_output(variant):
         lgn.check(lgn.lgn_forward_f32(*args))
     else:
         lgn.check(lgn.lgn_forward_twopass_f32(*args, out_ptr, M * N * 4))
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == 12345.0).all()) and bool((buf[pad + M * N:] == 12345.0).all())
+    y = buf[pad:pad + M * N].view(M, N).cpu().numpy()
+    assert max_err(y, oracle_rows(inp, G, 1e-5)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("N, G", [(480, 10), (1200, 6)], ids=["C48", "C200"])
+def test_twopass_masked_widths_write_nothing_outside(N, G):
+    # group widths of the masked epilogue, two rows per lane: with an odd M
+    # the last unit has one row, and nothing past the output may be written
+    M, K = 131, 32
+    log("two-pass bounds case M=%d K=%d N=%d G=%d" % (M, K, N, G))
+    inp = case(M, K, N, G, 24)
+    dev = to_device(inp, "f32")
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
+    out_ptr = buf.data_ptr() + pad * 4
+    lgn.check(lgn.lgn_forward_twopass_f32(dev["x"], dev["W"], dev["b_lin"], dev["b_add"],
+                                          dev["gamma"], dev["beta"], M, K, N, G, 1e-5, out_ptr,
+                                          out_ptr, M * N * 4))
     torch.cuda.synchronize()
     assert bool((buf[:pad] == 12345.0).all()) and bool((buf[pad + M * N:] == 12345.0).all())
     y = buf[pad:pad + M * N].view(M, N).cpu().numpy()
