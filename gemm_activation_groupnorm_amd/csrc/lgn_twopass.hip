@@ -63,7 +63,7 @@ static hipError_t launch_vec(const float *z, const float *b_add, const float *ga
                          stream, z, b_add, gamma, beta, (long long)M, G, eps, out);
 }
 
-template <int LPG, int V, int R = 1>
+template <int LPG, int V, int R, int EW>
 static hipError_t launch_masked(const float *z, const float *b_add, const float *gamma,
                                 const float *beta, int M, int G, int cg, float eps, float *out,
                                 hipStream_t stream) {
@@ -72,35 +72,36 @@ static hipError_t launch_masked(const float *z, const float *b_add, const float 
     const long long units = ((long long)M + R - 1) / R * G;
     const long long blocks = (units + per_block - 1) / per_block;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    return launch_kernel(lgn_gn_epilogue_masked_kernel<LPG, V, R>, dim3((unsigned)blocks),
+    return launch_kernel(lgn_gn_epilogue_masked_kernel<LPG, V, R, EW>, dim3((unsigned)blocks),
                          dim3(64), stream, z, b_add, gamma, beta, (long long)M, G, cg, eps, out);
 }
 
-// Group widths that are a multiple of 4 up to 4096 but not 4*LPG*V: the
-// masked vectorised kernel with the fewest lanes (F <= 64 float4s per group,
-// two rows per lane) or the fewest float4s per lane (above, one row per
-// lane) that cover the group.  Two rows per lane measured about 10 % faster
-// at 48, 96 and 200 channels and 2.5 % slower at 768.
+// Group widths not of the form 4*LPG*V, in slots of EW channels (F = cg/EW
+// slots per group, at most 1024): the masked kernel with the fewest lanes
+// (F <= 64) or the fewest slots per lane (above) that cover the group, two
+// rows per lane except for float4 slots above 64 per group.  Two rows per
+// lane measured about 10 % faster at 48, 96 and 200 channels and 2.5 %
+// slower at 768 (float4 slots).  Two-float slots against one-float slots:
+// 0.676 -> 0.362 ms at 50 channels, 0.408 -> 0.317 ms at 250 (32768 rows).
+template <int EW>
 static hipError_t launch_masked_any(const float *z, const float *b_add, const float *gamma,
                                     const float *beta, int M, int G, int cg, float eps,
                                     float *out, hipStream_t stream) {
-    const int F = cg / 4;
-    if (F <= 2)
-        return launch_masked<2, 1, 2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    if (F <= 4)
-        return launch_masked<4, 1, 2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    if (F <= 8)
-        return launch_masked<8, 1, 2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    if (F <= 16)
-        return launch_masked<16, 1, 2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    if (F <= 32)
-        return launch_masked<32, 1, 2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    if (F <= 64)
-        return launch_masked<64, 1, 2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    if (F <= 128) return launch_masked<64, 2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    if (F <= 256) return launch_masked<64, 4>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    if (F <= 512) return launch_masked<64, 8>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-    return launch_masked<64, 16>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
+    const int F = cg / EW;
+#define LGN_MASKED(LPG, V, R) \
+    launch_masked<LPG, V, R, EW>(z, b_add, gamma, beta, M, G, cg, eps, out, stream)
+    if (F <= 2) return LGN_MASKED(2, 1, 2);
+    if (F <= 4) return LGN_MASKED(4, 1, 2);
+    if (F <= 8) return LGN_MASKED(8, 1, 2);
+    if (F <= 16) return LGN_MASKED(16, 1, 2);
+    if (F <= 32) return LGN_MASKED(32, 1, 2);
+    if (F <= 64) return LGN_MASKED(64, 1, 2);
+    constexpr int RB = EW == 4 ? 1 : 2;
+    if (F <= 128) return LGN_MASKED(64, 2, RB);
+    if (F <= 256) return LGN_MASKED(64, 4, RB);
+    if (F <= 512) return LGN_MASKED(64, 8, RB);
+    return LGN_MASKED(64, 16, RB);
+#undef LGN_MASKED
 }
 
 hipError_t launch_gn_epilogue(const float *z, const float *b_add, const float *gamma,
@@ -120,7 +121,11 @@ hipError_t launch_gn_epilogue(const float *z, const float *b_add, const float *g
         case 1024: return launch_vec<64, 4>(z, b_add, gamma, beta, M, G, eps, out, stream);
         default: {
             if (cg % 4 == 0 && cg <= 4096)
-                return launch_masked_any(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
+                return launch_masked_any<4>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
+            if (cg % 4 != 0 && cg % 2 == 0 && cg <= 2048)
+                return launch_masked_any<2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
+            if (cg % 2 != 0 && cg <= 1024)
+                return launch_masked_any<1>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
             if (pairs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
             return launch_kernel(lgn_gn_epilogue_generic_kernel, dim3((unsigned)pairs), dim3(64),
                                  stream, z, b_add, gamma, beta, pairs, G, cg, eps, out);

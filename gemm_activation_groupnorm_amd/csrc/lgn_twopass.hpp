@@ -178,18 +178,20 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_vec_kernel(
     }
 }
 
-// Epilogue for a group width CG that is a multiple of 4 but not of the form
-// 4*LPG*V: the vectorised kernel's layout with the slots past the group's
-// F = CG/4 float4s masked off (LPG >= F when V == 1, else LPG = 64 and
-// 64*V >= F), for R rows per lane: unit q = (block of R rows, group g),
-// q = rb*G + g, one load of b_add, gamma and beta serving the R rows.  A
-// lane's count of values varies (0 for a lane with no slot), so the merges
-// across the LPG lanes carry counts: Chan's update, lower lane first, so both
-// lanes of a pair hold the same bits.
-template <int LPG, int V, int R>
+// Epilogue for a group width CG not of the form 4*LPG*V: the vectorised
+// kernel's layout in slots of EW consecutive channels (EW = 4, a float4, when
+// CG % 4 == 0; 2 when CG % 2 == 0; else 1), with the slots past the group's
+// F = CG/EW masked
+// off (LPG >= F when V == 1, else LPG = 64 and 64*V >= F), for R rows per
+// lane: unit q = (block of R rows, group g), q = rb*G + g, one load of b_add,
+// gamma and beta serving the R rows.  A lane's count of values varies (0 for
+// a lane with no slot), so the merges across the LPG lanes carry counts:
+// Chan's update, lower lane first, so both lanes of a pair hold the same bits.
+template <int LPG, int V, int R, int EW>
 __global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
     const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
     const float *__restrict__ beta, long long M, int G, int CG, float eps, float *out) {
+    static_assert(EW == 1 || EW == 2 || EW == 4, "slots of one, two or four floats");
     constexpr int UPW = 64 / LPG;   // units per wave
     const int lane = threadIdx.x & 63;
     const long long units = (M + R - 1) / R * G;
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
     const bool live = q < units;
     const long long r0 = live ? (long long)R * (q / G) : 0;
     const int g = live ? (int)(q % G) : 0;
-    const int F = CG / 4;
+    const int F = CG / EW;
     size_t base[R];
     bool valid[R];
 #pragma unroll
@@ -206,8 +208,21 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
         valid[r] = live && r0 + r < M;
         base[r] = ((size_t)(valid[r] ? r0 + r : r0) * G + g) * CG;   // a missing row reads row r0
     }
+    auto load = [&](const float *p, float (&d)[EW]) {
+        if constexpr (EW == 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = t[e];
+        } else if constexpr (EW == 2) {
+            const float2 t = *reinterpret_cast<const float2 *>(p);
+            d[0] = t.x;
+            d[1] = t.y;
+        } else {
+            d[0] = *p;
+        }
+    };
 
-    f32x4 u[R][V];
+    float u[R][V][EW];
     float sum[R], n = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) sum[r] = 0.f;
@@ -215,24 +230,30 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
     for (int v = 0; v < V; ++v) {
         const int f = j + LPG * v;
         const bool in = live && f < F;
-        f32x4 ba = {0.f, 0.f, 0.f, 0.f};
-        if (in) {
-            const int ch = g * CG + 4 * f;
+        float ba[EW];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ba[e] = b_add[ch + e];
-            n += 4.f;
+        for (int e = 0; e < EW; ++e) ba[e] = 0.f;
+        if (in) {
+            const int ch = g * CG + EW * f;
+#pragma unroll
+            for (int e = 0; e < EW; ++e) ba[e] = b_add[ch + e];
+            n += (float)EW;
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            f32x4 val = {0.f, 0.f, 0.f, 0.f};
+            float val[EW];
+#pragma unroll
+            for (int e = 0; e < EW; ++e) val[e] = 0.f;
             if (in) {
-                val = *reinterpret_cast<const f32x4 *>(z + base[r] + 4 * f);
+                load(z + base[r] + EW * f, val);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = swish(val[e]) + ba[e];
+                for (int e = 0; e < EW; ++e) val[e] = swish(val[e]) + ba[e];
             }
-            u[r][v] = val;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sum[r] += val[e];
+            for (int e = 0; e < EW; ++e) {
+                u[r][v][e] = val[e];
+                sum[r] += val[e];
+            }
         }
     }
     float mean[R], rstd[R];
@@ -244,7 +265,7 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
         for (int v = 0; v < V; ++v)
             if (j + LPG * v < F) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < EW; ++e) {
                     const float d = u[r][v][e] - mn;
                     m2 += d * d;
                 }
@@ -279,19 +300,29 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
     for (int v = 0; v < V; ++v) {
         const int f = j + LPG * v;
         if (f < F) {
-            const int ch = g * CG + 4 * f;
-            float ga[4], be[4];
+            const int ch = g * CG + EW * f;
+            float ga[EW], be[EW];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < EW; ++e) {
                 ga[e] = gamma[ch + e];
                 be[e] = beta[ch + e];
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                f32x4 y;
+                if (!valid[r]) continue;
+                if constexpr (EW == 4) {
+                    f32x4 y;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = (u[r][v][e] - mean[r]) * rstd[r] * ga[e] + be[e];
-                if (valid[r]) *reinterpret_cast<f32x4 *>(out + base[r] + 4 * f) = y;
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = (u[r][v][e] - mean[r]) * rstd[r] * ga[e] + be[e];
+                    *reinterpret_cast<f32x4 *>(out + base[r] + 4 * f) = y;
+                } else if constexpr (EW == 2) {
+                    *reinterpret_cast<float2 *>(out + base[r] + 2 * f) =
+                        make_float2((u[r][v][0] - mean[r]) * rstd[r] * ga[0] + be[0],
+                                    (u[r][v][1] - mean[r]) * rstd[r] * ga[1] + be[1]);
+                } else {
+                    out[base[r] + f] = (u[r][v][0] - mean[r]) * rstd[r] * ga[0] + be[0];
+                }
             }
         }
     }
@@ -299,8 +330,9 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
 
 // Epilogue, any channel count: one wave per (row, group), three passes over
 // the group (sum; sum of squared deviations from the mean; normalise), each
-// an xor-butterfly sum over the wave.  Used when C is not a multiple of 4 or
-// is above 4096.
+// an xor-butterfly sum over the wave.  Used for groups wider than the masked
+// kernel covers (1024 slots: 4096 channels when C % 4 == 0, 2048 when C % 2
+// == 0, else 1024).
 __global__ __launch_bounds__(64) void lgn_gn_epilogue_generic_kernel(
     const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
     const float *__restrict__ beta, long long pairs, int G, int CG, float eps, float *out) {
