@@ -252,10 +252,12 @@ def test_no_writes_outside_output(variant):
     assert max_err(y, oracle_rows(inp, G, 1e-5)) <= TOL["f32"]
 
 
-@pytest.mark.parametrize("N, G", [(480, 10), (1200, 6)], ids=["C48", "C200"])
+@pytest.mark.parametrize("N, G", [(480, 10), (1200, 6), (500, 10), (100, 4)],
+                         ids=["C48", "C200", "C50", "C25"])
 def test_twopass_masked_widths_write_nothing_outside(N, G):
-    # group widths of the masked epilogue, two rows per lane: with an odd M
-    # the last unit has one row, and nothing past the output may be written
+    # group widths of the masked epilogue (float4, float2 and one-float slots),
+    # two rows per lane, in place: with an odd M the last unit has one row, and
+    # nothing past the output may be written
     M, K = 131, 32
     log("two-pass bounds case M=%d K=%d N=%d G=%d" % (M, K, N, G))
     inp = case(M, K, N, G, 24)
