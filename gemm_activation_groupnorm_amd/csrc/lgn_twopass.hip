@@ -77,9 +77,10 @@ static hipError_t launch_masked(const float *z, const float *b_add, const float 
 }
 
 // Group widths not of the form 4*LPG*V, in slots of EW channels (F = cg/EW
-// slots per group, at most 1024): the masked kernel with the fewest lanes
+// slots per group, at most 2048): the masked kernel with the fewest lanes
 // (F <= 64) or the fewest slots per lane (above) that cover the group, two
-// rows per lane except for float4 slots above 64 per group.  Two rows per
+// rows per lane except for float4 slots above 64 per group and for 32 slots
+// per lane.  Two rows per
 // lane measured about 10 % faster at 48, 96 and 200 channels and 2.5 %
 // slower at 768 (float4 slots).  Two-float slots against one-float slots:
 // 0.676 -> 0.362 ms at 50 channels, 0.408 -> 0.317 ms at 250 (32768 rows).
@@ -100,7 +101,8 @@ static hipError_t launch_masked_any(const float *z, const float *b_add, const fl
     if (F <= 128) return LGN_MASKED(64, 2, RB);
     if (F <= 256) return LGN_MASKED(64, 4, RB);
     if (F <= 512) return LGN_MASKED(64, 8, RB);
-    return LGN_MASKED(64, 16, RB);
+    if (F <= 1024) return LGN_MASKED(64, 16, RB);
+    return LGN_MASKED(64, 32, 1);
 #undef LGN_MASKED
 }
 
@@ -120,11 +122,11 @@ hipError_t launch_gn_epilogue(const float *z, const float *b_add, const float *g
         case 512: return launch_vec<64, 2>(z, b_add, gamma, beta, M, G, eps, out, stream);
         case 1024: return launch_vec<64, 4>(z, b_add, gamma, beta, M, G, eps, out, stream);
         default: {
-            if (cg % 4 == 0 && cg <= 4096)
+            if (cg % 4 == 0 && cg <= 8192)
                 return launch_masked_any<4>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-            if (cg % 4 != 0 && cg % 2 == 0 && cg <= 2048)
+            if (cg % 4 != 0 && cg % 2 == 0 && cg <= 4096)
                 return launch_masked_any<2>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
-            if (cg % 2 != 0 && cg <= 1024)
+            if (cg % 2 != 0 && cg <= 2048)
                 return launch_masked_any<1>(z, b_add, gamma, beta, M, G, cg, eps, out, stream);
             if (pairs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
             return launch_kernel(lgn_gn_epilogue_generic_kernel, dim3((unsigned)pairs), dim3(64),

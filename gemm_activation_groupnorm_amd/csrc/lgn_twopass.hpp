@@ -331,8 +331,8 @@ __global__ __launch_bounds__(64) void lgn_gn_epilogue_masked_kernel(
 // Epilogue, any channel count: one wave per (row, group), three passes over
 // the group (sum; sum of squared deviations from the mean; normalise), each
 // an xor-butterfly sum over the wave.  Used for groups wider than the masked
-// kernel covers (1024 slots: 4096 channels when C % 4 == 0, 2048 when C % 2
-// == 0, else 1024).
+// kernel covers (2048 slots: 8192 channels when C % 4 == 0, 4096 when C % 2
+// == 0, else 2048).
 __global__ __launch_bounds__(64) void lgn_gn_epilogue_generic_kernel(
     const float *z, const float *__restrict__ b_add, const float *__restrict__ gamma,
     const float *__restrict__ beta, long long pairs, int G, int CG, float eps, float *out) {

@@ -90,16 +90,19 @@ def test_shapes(shape, dtype, variant):
                                    (9, 32, 2048, 1), (12, 40, 1200, 10),
                                    # C a multiple of 4 but not a power of two: 48, 96, 200,
                                    # 768 (three float4s per lane, one slot masked), 4096;
-                                   # C even but not a multiple of 4 (two-float slots): 50,
-                                   # 6, 250, 1000, 2042; C odd (one-float slots): 3 (above),
-                                   # 25, 125, 1023; then 6144, 2050 and 1025, which take
-                                   # the generic kernel
+                                   # 6144 and 8192 (32 float4s per lane); C even but not a
+                                   # multiple of 4 (two-float slots): 50, 6, 250, 1000,
+                                   # 2042, 2050, 4094; C odd (one-float slots): 3 (above),
+                                   # 25, 125, 1023, 1025, 2047; then 16384, 4098 and 2049,
+                                   # which take the generic kernel
                                    (33, 32, 480, 10), (29, 24, 768, 8), (17, 40, 4000, 20),
-                                   (13, 16, 3072, 4), (7, 32, 4096, 1), (21, 16, 100, 2),
-                                   (15, 8, 36, 6), (11, 24, 500, 2), (9, 16, 2000, 2),
-                                   (5, 16, 4084, 2), (19, 8, 100, 4), (7, 16, 1000, 8),
-                                   (5, 8, 4092, 4), (5, 8, 12288, 2), (6, 8, 4100, 2),
-                                   (4, 8, 4100, 4)],
+                                   (13, 16, 3072, 4), (7, 32, 4096, 1), (5, 8, 12288, 2),
+                                   (3, 8, 8192, 1), (21, 16, 100, 2), (15, 8, 36, 6),
+                                   (11, 24, 500, 2), (9, 16, 2000, 2), (5, 16, 4084, 2),
+                                   (6, 8, 4100, 2), (3, 8, 8188, 2), (19, 8, 100, 4),
+                                   (7, 16, 1000, 8), (5, 8, 4092, 4), (4, 8, 4100, 4),
+                                   (3, 8, 8188, 4), (2, 8, 16384, 1), (3, 8, 8196, 2),
+                                   (3, 8, 8196, 4)],
                          ids=lambda s: "M%d_K%d_N%d_G%d" % s)
 def test_twopass_other_group_widths(shape, dtype):
     M, K, N, G = shape
