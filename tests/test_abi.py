@@ -478,3 +478,23 @@ def test_header_compiles_as_c_and_links(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_header_compiles_as_cxx_and_links(tmp_path):
+    """The same C program built as C++17 (the header's extern "C" block), linked
+    against liblgn.so: the names resolve without C++ mangling."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no g++")
+    pkg = os.path.dirname(lgn.LIB_PATH)
+    exe = str(tmp_path / "cxx_abi_check")
+    cmd = [gxx, "-x", "c++", "-std=c++17", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "c_abi_check.c"), "-x", "none", "-L", pkg, "-llgn",
+           "-Wl,-rpath," + pkg, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
